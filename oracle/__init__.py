@@ -1,0 +1,15 @@
+"""CPU oracle (float64, numpy) of the StateKV streaming video-prefill step.
+
+Test infrastructure only: the test suite, the build entry point's smoke check
+and the benchmark's CPU-baseline leg may import it; the GPU library never does.
+"""
+
+from .statekv_oracle import (  # noqa: F401
+    FrameResult,
+    StateKVOracle,
+    decode_bf16,
+    frame_attention,
+    full_causal_attention,
+    importance_scores,
+    select_top_b,
+)

@@ -1,0 +1,205 @@
+"""Checks that pin the CPU oracle to facts fixed outside itself.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with a value
+worked out by hand, a closed form, an invariant, a library routine or brute
+force.  The same checks run against deliberately broken copies of the oracle
+(see test_oracle_mutations.py) to show that each plausible mistake is caught.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.statekv_oracle as so
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _frac(s: str) -> float:
+    return float(Fraction(s))
+
+
+def check_hand_example() -> None:
+    """Three-frame example worked by hand with exact rationals (tests/golden)."""
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    orc = so.StateKVOracle(ex["n_q_heads"], ex["n_kv_heads"], ex["head_dim"],
+                           ex["frame_tokens"], ex["state_budget"], scale=math.log(2.0))
+    for fr, exp in zip(ex["frames"], ex["expected"]):
+        q = np.array(fr["q"], dtype=np.float64)[:, None, :]
+        k = np.array(fr["k"], dtype=np.float64)[:, None, :]
+        v = np.array(fr["v"], dtype=np.float64)[:, None, :]
+        res = orc.step(q, k, v)
+        o_exp = np.array([[_frac(x) for x in row] for row in exp["o"]])
+        np.testing.assert_allclose(res.o[:, 0, :], o_exp, rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(res.pool_positions[0], exp["pool_positions"])
+        np.testing.assert_allclose(res.scores[0], [_frac(x) for x in exp["scores"]],
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(res.kept_positions[0], exp["kept_positions"])
+
+
+def check_single_token_frame() -> None:
+    """T = 1 with an empty state: the only visible key is the token itself, O = v."""
+    rng = np.random.default_rng(7)
+    orc = so.StateKVOracle(4, 2, 8, 1, 3)
+    q = rng.standard_normal((1, 4, 8))
+    k = rng.standard_normal((1, 2, 8))
+    v = rng.standard_normal((1, 2, 8))
+    res = orc.step(q, k, v)
+    for g in range(4):
+        np.testing.assert_allclose(res.o[0, g], v[0, g // 2], rtol=0, atol=1e-15)
+    for h in range(2):
+        np.testing.assert_allclose(res.scores[h], [2.0], rtol=0, atol=1e-15)
+
+
+def check_uniform_attention_closed_form() -> None:
+    """All keys zero: every visible key gets weight 1/(number visible).
+
+    Query t of frame n sees c + t + 1 keys, so O_t is the mean of those values,
+    and a state key's importance is G * sum_t 1/(c+t+1); frame key t' gets
+    G * sum_{t>=t'} 1/(c+t+1).  Pins the causal mask, the state visibility and
+    the score definition (sum, not mean, over queries and the group's heads).
+    """
+    rng = np.random.default_rng(11)
+    Hq, Hkv, d, T, B = 6, 2, 4, 5, 7
+    G = Hq // Hkv
+    orc = so.StateKVOracle(Hq, Hkv, d, T, B)
+    for n in range(3):
+        q = rng.standard_normal((T, Hq, d))
+        k = np.zeros((T, Hkv, d))
+        v = rng.standard_normal((T, Hkv, d))
+        prev_pos = [orc.state(h)[0].copy() for h in range(Hkv)]
+        prev_v = [None if orc.state(h)[2] is None else orc.state(h)[2].copy()
+                  for h in range(Hkv)]
+        res = orc.step(q, k, v)
+        for h in range(Hkv):
+            c = prev_pos[h].shape[0]
+            pool_v = v[:, h, :] if c == 0 else np.concatenate([prev_v[h], v[:, h, :]])
+            for t in range(T):
+                mean = pool_v[: c + t + 1].mean(axis=0)
+                for g in range(h * G, (h + 1) * G):
+                    np.testing.assert_allclose(res.o[t, g], mean, rtol=0, atol=1e-13)
+            expect = np.zeros(c + T)
+            for t in range(T):
+                expect[: c + t + 1] += G / (c + t + 1)
+            np.testing.assert_allclose(res.scores[h], expect, rtol=0, atol=1e-13)
+
+
+def check_gqa_head_mapping() -> None:
+    """Query head g reads KV head floor(g/G): make KV head 1's keys zero and its
+    values constant per head; heads G..2G-1 must output that constant."""
+    rng = np.random.default_rng(5)
+    Hq, Hkv, d, T = 6, 3, 8, 4
+    G = Hq // Hkv
+    orc = so.StateKVOracle(Hq, Hkv, d, T, 16)
+    q = rng.standard_normal((T, Hq, d)) * 3
+    k = rng.standard_normal((T, Hkv, d)) * 3
+    v = rng.standard_normal((T, Hkv, d))
+    for h in range(Hkv):
+        v[:, h, :] = float(h + 1)
+    res = orc.step(q, k, v)
+    for g in range(Hq):
+        np.testing.assert_allclose(res.o[:, g, :], float(g // G + 1), rtol=0, atol=1e-13)
+
+
+def check_probability_invariants() -> None:
+    """Rows of P sum to 1; each KV head's scores sum to G*T (every query spends
+    a total weight of 1); the scores equal column sums of P built by explicit
+    scalar loops with math.exp."""
+    rng = np.random.default_rng(3)
+    Hq, Hkv, d, T, B = 4, 2, 6, 3, 4
+    G = Hq // Hkv
+    orc = so.StateKVOracle(Hq, Hkv, d, T, B, scale=0.7)
+    for n in range(3):
+        q = rng.standard_normal((T, Hq, d))
+        k = rng.standard_normal((T, Hkv, d))
+        v = rng.standard_normal((T, Hkv, d))
+        st = [orc.state(h) for h in range(Hkv)]
+        st = [(p.copy(), None if kk is None else kk.copy()) for p, kk, _ in st]
+        res = orc.step(q, k, v, keep_probs=True)
+        for P in res.probs:
+            np.testing.assert_allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+        for h in range(Hkv):
+            np.testing.assert_allclose(res.scores[h].sum(), G * T, rtol=1e-14)
+            c = st[h][0].shape[0]
+            pool_k = k[:, h, :] if c == 0 else np.concatenate([st[h][1], k[:, h, :]])
+            col = [0.0] * (c + T)
+            for g in range(h * G, (h + 1) * G):
+                for t in range(T):
+                    visible = list(range(c + t + 1))
+                    logits = [0.7 * sum(q[t, g, e] * pool_k[j, e] for e in range(d))
+                              for j in visible]
+                    mx = max(logits)
+                    w = [math.exp(z - mx) for z in logits]
+                    tot = sum(w)
+                    for j, wj in zip(visible, w):
+                        col[j] += wj / tot
+            np.testing.assert_allclose(res.scores[h], col, rtol=0, atol=1e-13)
+
+
+def check_full_attention_equivalence(n_frames: int = 8) -> None:
+    """B >= every history: nothing is evicted, so each frame's output equals
+    dense causal self-attention over the whole video so far."""
+    rng = np.random.default_rng(9)
+    Hq, Hkv, d, T = 4, 2, 16, 8
+    B = T * n_frames
+    orc = so.StateKVOracle(Hq, Hkv, d, T, B)
+    qs, ks, vs = [], [], []
+    for n in range(n_frames):
+        q = rng.standard_normal((T, Hq, d))
+        k = rng.standard_normal((T, Hkv, d))
+        v = rng.standard_normal((T, Hkv, d))
+        qs.append(q), ks.append(k), vs.append(v)
+        res = orc.step(q, k, v)
+        ref = so.full_causal_attention(q, np.concatenate(ks), np.concatenate(vs),
+                                       first_query=n * T)
+        np.testing.assert_allclose(res.o, ref, rtol=0, atol=1e-12)
+
+
+def check_selection_and_caches() -> None:
+    """Eviction keeps exactly B tokens once the pool exceeds B; the kept set is
+    the top-B by (score desc, position asc); every state row is bit-identical
+    to the frame row it came from; the detailed state holds every frame row."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, d, T, B = 4, 2, 8, 5, 7
+    orc = so.StateKVOracle(Hq, Hkv, d, T, B)
+    all_k, all_v = [], []
+    for n in range(6):
+        q = rng.standard_normal((T, Hq, d)).astype(np.float32)
+        k = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+        v = rng.standard_normal((T, Hkv, d)).astype(np.float32)
+        all_k.append(k), all_v.append(v)
+        res = orc.step(q, k, v)
+        for h in range(Hkv):
+            pool = res.pool_positions[h]
+            assert res.kept_positions[h].shape[0] == min(B, (n + 1) * T)
+            if pool.shape[0] > B:
+                order = sorted(range(pool.shape[0]),
+                               key=lambda j: (-res.scores[h][j], pool[j]))
+                np.testing.assert_array_equal(res.kept_positions[h],
+                                              np.sort(pool[order[:B]]))
+            pos, ck, cv = orc.state(h)
+            K = np.concatenate(all_k)[:, h, :]
+            V = np.concatenate(all_v)[:, h, :]
+            assert ck.dtype == np.float32
+            np.testing.assert_array_equal(ck, K[pos])
+            np.testing.assert_array_equal(cv, V[pos])
+            dpos, dk, dv = orc.detailed(h)
+            np.testing.assert_array_equal(dpos, np.arange((n + 1) * T))
+            np.testing.assert_array_equal(dk, K)
+            np.testing.assert_array_equal(dv, V)
+
+
+ALL_CHECKS = [
+    check_hand_example,
+    check_single_token_frame,
+    check_uniform_attention_closed_form,
+    check_gqa_head_mapping,
+    check_probability_invariants,
+    check_full_attention_equivalence,
+    check_selection_and_caches,
+]

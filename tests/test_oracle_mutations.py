@@ -1,0 +1,119 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and show the pins catch them.
+
+Each mutant replaces one function of the oracle module for the duration of a
+test; at least one of the pins in oracle_pins must then fail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.statekv_oracle as so
+import oracle_pins
+
+_orig_attention = so.frame_attention
+_orig_scores = so.importance_scores
+_orig_select = so.select_top_b
+
+
+def attention_causal_off_by_one(q, keys, values, n_state, scale, causal=True):
+    T = q.shape[0]
+    z = scale * (q @ keys.T)
+    t = np.arange(T)
+    cols = np.arange(keys.shape[0] - n_state)
+    z[:, n_state:][cols[None, :] >= t[:, None]] = -np.inf   # hides the token itself
+    z[:, n_state:][0, 0] = 0.0 if T else 0.0                # keep row 0 finite
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    P = e / e.sum(axis=1, keepdims=True)
+    return P, P @ values
+
+
+def attention_mask_on_state_too(q, keys, values, n_state, scale, causal=True):
+    T = q.shape[0]
+    z = scale * (q @ keys.T)
+    # treat the whole pool as if it were the frame: state tokens become causal
+    cols = np.arange(keys.shape[0])
+    z[cols[None, :] > (np.arange(T)[:, None] + n_state // 2)] = -np.inf
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    P = e / e.sum(axis=1, keepdims=True)
+    return P, P @ values
+
+
+def attention_no_scale(q, keys, values, n_state, scale, causal=True):
+    return _orig_attention(q, keys, values, n_state, 1.0, causal)
+
+
+def attention_transposed_values(q, keys, values, n_state, scale, causal=True):
+    P, _ = _orig_attention(q, keys, values, n_state, scale, causal)
+    # uses the values of the reversed pool
+    return P, P @ values[::-1]
+
+
+def scores_mean_over_queries(P_heads):
+    return _orig_scores(P_heads) / P_heads[0].shape[0]
+
+
+def scores_first_head_only(P_heads):
+    return P_heads[0].sum(axis=0)
+
+
+def scores_row_sums_broadcast(P_heads):
+    # sums the wrong axis, then spreads it over the pool
+    s = sum(P.sum(axis=1).sum() for P in P_heads)
+    return np.full(P_heads[0].shape[1], s / P_heads[0].shape[1])
+
+
+def select_ties_to_higher_position(scores, positions, budget):
+    return _orig_select(scores, -np.asarray(positions), budget)[::-1]
+
+
+def select_smallest_scores(scores, positions, budget):
+    return _orig_select(-np.asarray(scores), positions, budget)
+
+
+def select_off_by_one_budget(scores, positions, budget):
+    return _orig_select(scores, positions, max(1, budget - 1))
+
+
+MUTANTS = [
+    ("frame_attention", attention_causal_off_by_one),
+    ("frame_attention", attention_mask_on_state_too),
+    ("frame_attention", attention_no_scale),
+    ("frame_attention", attention_transposed_values),
+    ("importance_scores", scores_mean_over_queries),
+    ("importance_scores", scores_first_head_only),
+    ("importance_scores", scores_row_sums_broadcast),
+    ("select_top_b", select_ties_to_higher_position),
+    ("select_top_b", select_smallest_scores),
+    ("select_top_b", select_off_by_one_budget),
+]
+
+
+@pytest.mark.parametrize("name,mutant", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, mutant):
+    monkeypatch.setattr(so, name, mutant)
+    failures = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            failures.append(check.__name__)
+    assert failures, f"no pin caught the mutant {mutant.__name__}"
+
+
+def test_gqa_mapping_mutant(monkeypatch):
+    """A wrong query-head -> KV-head mapping (g % Hkv instead of g // G)."""
+    orig_step = so.StateKVOracle.step
+
+    def step(self, q, k, v, keep_probs=False):
+        # permute query heads so head g is served by KV head g % Hkv
+        perm = np.array([(g % self.Hkv) * self.G + g // self.Hkv for g in range(self.Hq)])
+        res = orig_step(self, np.asarray(q)[:, perm, :], k, v, keep_probs)
+        inv = np.argsort(perm)
+        res.o = res.o[:, inv, :]
+        return res
+
+    monkeypatch.setattr(so.StateKVOracle, "step", step)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_gqa_head_mapping()
