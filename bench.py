@@ -1,0 +1,374 @@
+"""Benchmark of the StateKV per-layer video-prefill step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one frame through one layer: attention over [C_{n-1} ; frame]
+with importance scores, top-B select, gather of C_n and append to D (every
+row of the hot path).  Default workload: the InternVL3-8B-like layer
+(Hq=28, Hkv=4, d=128, T=256, B=4096), W=16 warm-up frames (they fill the
+state: 16*256 = B) and K=496 timed frames, i.e. the pages' 512-frame stream.
+All frames are generated on the host (seeded, synthetic) and staged in HBM
+before the timed region.
+
+Prints ONE JSON line: frames/s per layer, a roofline entry for the dominant
+kernel (its average launch time measured with HIP events on the launch
+stream during the timed region), the per-kernel breakdown and the float64
+CPU oracle timed on a bounded sample of the same stream.
+
+Other measurements (not the headline line):
+    --mode crossover   StateKV vs quadratic full attention, 1B shape,
+                       B in {1024, 2048, 4096}, N in {32, ..., 512}
+    --mode depth28     28 independent 2B-shaped layers, layer-major per
+                       frame, per-frame latency at frames 1, 9, 65, 256
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "internvl3_8b_layer"
+
+
+def _fail_multi_gpu(n):
+    print(json.dumps({"error": f"--gpus {n}: this benchmark runs on one GPU only; the "
+                               "StateKV step of a layer is measured on a single MI355X "
+                               "(see the sharding notes in DESIGN.md)."}))
+    sys.exit(2)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work per kernel launch
+# ----------------------------------------------------------------------------
+
+def visible_pairs(T: int, c: int, causal: bool = True) -> float:
+    """(query, key) pairs of one query head: every state key, the frame triangle."""
+    return T * c + (T * (T + 1) / 2 if causal else T * T)
+
+
+def attn_out_flops(Hq, d, T, c) -> float:
+    """Pass 2: QK^T (2d per pair) and PV (2d per pair) on MFMA."""
+    return 4.0 * Hq * d * visible_pairs(T, c)
+
+
+def attn_stats_flops(Hq, d, T, c) -> float:
+    """Pass 1: QK^T only."""
+    return 2.0 * Hq * d * visible_pairs(T, c)
+
+
+def useful_attention_flops(Hq, d, T, c) -> float:
+    """What the step needs once: QK^T + PV over the visible pairs."""
+    return 4.0 * Hq * d * visible_pairs(T, c)
+
+
+def gather_bytes(Hkv, d, T, B, c) -> float:
+    """C_n gather + D append, bytes that must cross HBM once.
+
+    Per kept row: read K and V (2*d*2 bytes) from C_{n-1} or the frame, write
+    them to C_n; read the selection index (4 B) and the old position (8 B),
+    write the position (8 B).  Append: read the frame's K and V rows, write
+    them to D."""
+    newc = min(B, c + T)
+    row = 2 * d * 2
+    gather = Hkv * newc * (2 * row + 4 + 8 + 8)
+    append = Hkv * T * 2 * row
+    return float(gather + append)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on host cores
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(spec, qs, ks, vs, warm: int, budget_s: float):
+    from threadpoolctl import threadpool_info
+
+    from oracle import StateKVOracle
+
+    orc = StateKVOracle(spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.frame_tokens,
+                        spec.state_budget)
+    for n in range(warm):
+        orc.step(qs[n], ks[n], vs[n])
+    t0 = time.perf_counter()
+    done = 0
+    n = warm
+    while n < qs.shape[0] and (done < 3 or time.perf_counter() - t0 < budget_s):
+        orc.step(qs[n], ks[n], vs[n])
+        n += 1
+        done += 1
+    dt = time.perf_counter() - t0
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {
+        "value": done / dt,
+        "unit": "frames/s per layer",
+        "cores": int(max(blas) if blas else 1),
+        "host_cores": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle, frames {warm}..{warm + done - 1} of the same "
+                   f"stream after it ran frames 0..{warm - 1} untimed; {dt:.1f} s"),
+    }
+
+
+# ----------------------------------------------------------------------------
+# traffic counters taken with rocprofv3 (committed under profiles/)
+# ----------------------------------------------------------------------------
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("streaming_long_video_amd/csrc/kernels/attention.hip",):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(kernel)
+    if not entry or entry.get("source_hash") != _kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+# headline: one layer, 512-frame stream
+# ----------------------------------------------------------------------------
+
+def run_headline(args):
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload(args.workload)
+    if spec.n_layers != 1:
+        raise SystemExit("the headline mode runs single-layer workloads")
+    W, K = args.warmup, args.steps
+    N = W + K
+    T, Hq, Hkv, d, Bs = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                         spec.state_budget)
+    t_gen = time.perf_counter()
+    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=min(16, os.cpu_count() or 1))
+    t_gen = time.perf_counter() - t_gen
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q_all, k_all, v_all = up(qs), up(ks), up(vs)
+    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T, num_splits=args.splits)
+    out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    for n in range(W):
+        layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+    torch.cuda.synchronize()
+
+    mask = {"none": 0, "dominant": 1 << 1, "all": (1 << len(skv.STATEKV_KERNELS)) - 1}[args.events]
+    skv.statekv_profile_start(layer.handle, mask, K * len(skv.STATEKV_KERNELS))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        layer.prefill(q_all[W + i], k_all[W + i], v_all[W + i], out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = skv.statekv_profile_stop(layer.handle)
+
+    cs = [min(Bs, n * T) for n in range(W, N)]
+    c_mean = float(np.mean(cs))
+    kernels_us = {k: (ms / cnt * 1e3 if cnt else None) for k, (ms, cnt) in prof.items()}
+    timed_kernels = {k: v for k, v in kernels_us.items() if v}
+    dominant = max(timed_kernels, key=timed_kernels.get) if timed_kernels else "attn_out"
+    flops = float(np.mean([attn_out_flops(Hq, d, T, c) for c in cs]))
+    result = {
+        "metric": "video-prefill frames/s per layer + % bf16 MFMA peak (8B shape, B=4096, T=256)",
+        "value": K / elapsed,
+        "unit": "frames/s per layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": elapsed / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, RoPE at original positions, "
+                "10 planted temporal-sink keys in frames 0-3)",
+        "config": {"workload": args.workload, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": d, "frame_tokens": T, "state_budget": Bs,
+                   "frames": N, "detailed_capacity": N * T},
+    }
+    att = kernels_us.get("attn_out")
+    if att:
+        achieved = flops / (att * 1e-6) / 1e12
+        result["roofline"] = {
+            "kernel": "attn_out (attention pass 2: QK^T recompute, P, PV, column sums)",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
+            "traffic": measured_traffic("attn_out"),
+            "flops_per_launch": flops, "avg_launch_us": att,
+        }
+    if kernels_us.get("attn_stats") and att:
+        useful = float(np.mean([useful_attention_flops(Hq, d, T, c) for c in cs]))
+        t_att = (kernels_us["attn_stats"] + att + (kernels_us.get("split_sum") or 0.0)) * 1e-6
+        result["attention"] = {
+            "useful_tflops": useful / t_att / 1e12,
+            "useful_frac_of_peak": useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
+            "executed_frac_of_peak": 1.5 * useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
+        }
+    if kernels_us.get("gather"):
+        gb = float(np.mean([gather_bytes(Hkv, d, T, Bs, c) for c in cs]))
+        result["gather_append"] = {
+            "bytes_per_launch": gb, "avg_launch_us": kernels_us["gather"],
+            "achieved_gbs": gb / (kernels_us["gather"] * 1e-6) / 1e9,
+            "frac_of_hbm_peak": gb / (kernels_us["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        }
+    result["kernels_us"] = kernels_us
+    result["dominant_kernel"] = dominant
+    result["event_mode"] = args.events
+    result["input_generation_s"] = t_gen
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, qs, ks, vs, W, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------------------
+# crossover sweep: StateKV vs quadratic full attention at the 1B shape
+# ----------------------------------------------------------------------------
+
+def run_crossover(args):
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload("crossover_1b")
+    T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+    Ns = [32, 64, 128, 256, 512]
+    Nmax = max(Ns)
+    qs, ks, vs = framegen.stacked_frames(spec, 0, Nmax, workers=min(16, os.cpu_count() or 1))
+    dev = torch.device("cuda", 0)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q_all, k_all, v_all = up(qs), up(ks), up(vs)
+    out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    rows = []
+    # StateKV: per-frame time of every frame (events around each call)
+    for B in (1024, 2048, 4096):
+        layer = skv.Layer(Hq, Hkv, d, T, B, detailed_capacity=Nmax * T)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(Nmax + 1)]
+        ev[0].record()
+        for n in range(Nmax):
+            layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+            ev[n + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([ev[n].elapsed_time(ev[n + 1]) for n in range(Nmax)])
+        for N in Ns:
+            steady = per[min(B // T + 1, N - 1):N]
+            rows.append({"method": "statekv", "B": B, "N": N,
+                         "ms_per_frame_steady": float(np.mean(steady)),
+                         "ms_last_frame": float(per[N - 1]),
+                         "ms_cumulative": float(per[:N].sum()),
+                         "gflop_last_frame": useful_attention_flops(Hq, d, T, min(B, (N - 1) * T))
+                         / 1e9,
+                         "gflop_cumulative": sum(useful_attention_flops(Hq, d, T, min(B, n * T))
+                                                 for n in range(N)) / 1e9})
+        layer.close()
+    # quadratic full attention: frame n attends over all n*T earlier tokens
+    layer = skv.Layer(Hq, Hkv, d, T, 1024, detailed_capacity=Nmax * T)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(Nmax + 1)]
+    ev[0].record()
+    for n in range(Nmax):
+        layer.full_attention(q_all[n], k_all[n], v_all[n], out=out)
+        ev[n + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[n].elapsed_time(ev[n + 1]) for n in range(Nmax)])
+    for N in Ns:
+        rows.append({"method": "full_attention", "N": N,
+                     "ms_last_frame": float(per[N - 1]),
+                     "ms_cumulative": float(per[:N].sum()),
+                     "gflop_last_frame": useful_attention_flops(Hq, d, T, (N - 1) * T) / 1e9,
+                     "gflop_cumulative": sum(useful_attention_flops(Hq, d, T, n * T)
+                                             for n in range(N)) / 1e9})
+    print(json.dumps({"mode": "crossover", "workload": "crossover_1b", "rows": rows}), flush=True)
+
+
+# ----------------------------------------------------------------------------
+# 28 layers of the 2B shape, layer-major per frame
+# ----------------------------------------------------------------------------
+
+def run_depth28(args):
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload("internvl3_2b_28layers")
+    T, Hq, Hkv, d, Bs = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                         spec.state_budget)
+    N, L = spec.n_frames, spec.n_layers
+    dev = torch.device("cuda", 0)
+    layers, frames = [], []
+    for l in range(L):
+        s = spec.for_layer(l)
+        qs, ks, vs = framegen.stacked_frames(s, 0, N, workers=min(16, os.cpu_count() or 1))
+        up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        frames.append((up(qs), up(ks), up(vs)))
+        layers.append(skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T))
+    out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
+    ev[0].record()
+    for n in range(N):
+        for l in range(L):
+            q, k, v = frames[l]
+            layers[l].prefill(q[n], k[n], v[n], out=out)
+        ev[n + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[n].elapsed_time(ev[n + 1]) for n in range(N)]
+    pick = {f"frame_{n + 1}": per[n] for n in (0, 8, 64, N - 1)}
+    print(json.dumps({"mode": "depth28", "workload": "internvl3_2b_28layers",
+                      "ms_per_frame_all_layers": pick,
+                      "ms_mean_steady": float(np.mean(per[Bs // T + 1:])),
+                      "ms_first_frame": per[0]}), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=496)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--mode", choices=["headline", "crossover", "depth28"], default="headline")
+    ap.add_argument("--events", choices=["none", "dominant", "all"], default="all",
+                    help="kernels bracketed by HIP events during the timed region")
+    ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))
+    if args.steps < 1 or args.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28}[args.mode](args)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,5 +16,6 @@ from .generator import (  # noqa: F401
     frames,
     rope_rotate,
     sink_plan,
+    stacked_frames,
     workload,
 )

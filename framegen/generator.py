@@ -215,3 +215,34 @@ def frames(spec: FrameSpec, start: int = 0, stop: Optional[int] = None
     plan = sink_plan(spec)
     for n in range(start, stop):
         yield frame(spec, n, plan)
+
+
+def _frame_job(args):
+    spec, n = args
+    return frame(spec, n)
+
+
+def stacked_frames(spec: FrameSpec, start: int = 0, stop: Optional[int] = None,
+                   workers: int = 1):
+    """Frames start..stop-1 stacked: q (N,T,Hq,d), k and v (N,T,Hkv,d), uint16.
+
+    With workers > 1 the frames are drawn in a process pool; every frame has
+    its own random stream, so the result does not depend on the worker count.
+    """
+    stop = spec.n_frames if stop is None else stop
+    n = stop - start
+    T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+    q = np.empty((n, T, Hq, d), dtype=np.uint16)
+    k = np.empty((n, T, Hkv, d), dtype=np.uint16)
+    v = np.empty((n, T, Hkv, d), dtype=np.uint16)
+    jobs = [(spec, i) for i in range(start, stop)]
+    if workers > 1 and n > 1:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(min(workers, n)) as pool:
+            for i, (a, b, c) in enumerate(pool.imap(_frame_job, jobs, chunksize=4)):
+                q[i], k[i], v[i] = a, b, c
+    else:
+        plan = sink_plan(spec)
+        for i, (_, m) in enumerate(jobs):
+            q[i], k[i], v[i] = frame(spec, m, plan)
+    return q, k, v

@@ -1,0 +1,200 @@
+/*
+ * statekv.h -- C ABI of the StateKV streaming video-prefill step on MI355X (gfx950).
+ *
+ * What the library computes (per transformer layer, per arriving frame n):
+ *   1. the frame's T queries attend, with a softmax, over the candidate pool
+ *      [compressed state C_{n-1} ; the frame's own T keys/values]; every state
+ *      token is visible to every query, frame tokens are causal (t' <= t);
+ *   2. the same probabilities give every candidate j an importance score
+ *      sigma_j = sum over the frame's queries i and over the query heads that
+ *      share j's KV head of P_ij;
+ *   3. the top-B candidates by (sigma descending, original position ascending)
+ *      become C_n;
+ *   4. the frame's keys/values are appended to the detailed cache D_n.
+ * Sources: "Linear Scaling Video VLMs for Long Video Understanding" as
+ * summarised on paper.rainbus.top (method-steps section: per-layer detailed and
+ * fixed-capacity compressed states, attention over their concatenation, append
+ * to the detailed state, top-B of previous state plus frame by summed attention
+ * weight) and on paperlayer.ai (section 3.2-3.3: the two caches and the
+ * per-frame cache-builder pass; App. A "Protocol": sinks are kept per layer and
+ * KV head).  The pages define no programming interface; this one is derived
+ * from that description.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are device pointers (hipMalloc'd or torch CUDA memory),
+ *     contiguous, 16-byte aligned.  bf16 means IEEE bfloat16 bit patterns.
+ *   - Q is [T][Hq][d] bf16, K and V are [T][Hkv][d] bf16 (token-major, the
+ *     natural output of a QKV projection), already rotated (RoPE) at the tokens'
+ *     original positions p = position_offset + n*T + t.  The library never
+ *     applies positional encoding; it only records p.
+ *   - O is written as float32 [T][Hq][d].
+ *   - `stream` is a hipStream_t (NULL = default stream).  Work is enqueued
+ *     asynchronously; results are ready once the stream is synchronised.
+ *   - The caller owns every device buffer, including the one workspace; the
+ *     library never allocates device memory.  The layer handle is host memory
+ *     owned by the library until statekv_free_layer.
+ *   - Every argument check is done on the host before anything is enqueued; on
+ *     an error return other than STATEKV_ERR_HIP nothing was enqueued and the
+ *     layer is unchanged.
+ *     Asynchronous device faults surface at the caller's next synchronisation.
+ *   - A layer is not thread-safe; use one layer per stream.  Distinct layers are
+ *     independent.
+ */
+#ifndef STATEKV_H_
+#define STATEKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning entry point. */
+enum {
+  STATEKV_OK = 0,
+  STATEKV_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad shape, misuse          */
+  STATEKV_ERR_UNSUPPORTED = -2,      /* valid but not implemented (e.g. d=96)    */
+  STATEKV_ERR_WORKSPACE = -3,        /* workspace too small or misaligned        */
+  STATEKV_ERR_CAPACITY = -4,         /* detailed cache full and D_RING not set   */
+  STATEKV_ERR_HIP = -5               /* a HIP launch reported an error           */
+};
+
+/* Layer flags. */
+enum {
+  /* Not implemented in this version (returns STATEKV_ERR_UNSUPPORTED): one
+   * kept set per layer from scores summed over all query heads.  The default is
+   * per-KV-head selection (paperlayer App. A: sinks kept per layer and KV head). */
+  STATEKV_FLAG_SELECT_SHARED = 1u << 0,
+  /* Wrap the detailed cache: token p goes to slot (p - position_offset) mod
+   * detailed_capacity.  Without it, a frame that would overflow D fails with
+   * STATEKV_ERR_CAPACITY. */
+  STATEKV_FLAG_D_RING = 1u << 1,
+  /* Frame tokens see every frame token, not only earlier ones. */
+  STATEKV_FLAG_NONCAUSAL_FRAME = 1u << 2
+};
+
+typedef struct statekv_layer statekv_layer; /* opaque, host memory */
+
+typedef struct statekv_layer_config {
+  int32_t n_q_heads;         /* Hq, multiple of n_kv_heads, G = Hq/Hkv <= 16     */
+  int32_t n_kv_heads;        /* Hkv >= 1                                         */
+  int32_t head_dim;          /* d: 64 or 128                                     */
+  int32_t frame_tokens;      /* T, 1 .. 4096                                     */
+  int32_t state_budget;      /* B >= 1 with B + T <= 32768                       */
+  int32_t num_splits;        /* key splits of the attention grid; 0 = automatic  */
+  int64_t detailed_capacity; /* tokens preallocated per KV head in D, >= T       */
+  int64_t position_offset;   /* original position of frame 0, token 0            */
+  float softmax_scale;       /* logit scale; <= 0 means 1/sqrt(d)                */
+  uint32_t flags;            /* STATEKV_FLAG_*                                   */
+} statekv_layer_config;
+
+/* View of the compressed state C_n (borrowed; valid until the next
+ * prefill/reset/free on the layer).  Rows [0, count) of every KV head are live,
+ * in ascending original position.  Read after synchronising the stream. */
+typedef struct statekv_state_view {
+  const void* k;            /* device, [Hkv][capacity][d] bf16                   */
+  const void* v;            /* device, [Hkv][capacity][d] bf16                   */
+  const int64_t* pos;       /* device, [Hkv][capacity] original positions        */
+  const float* last_scores; /* device, [Hkv][scores_stride]: importance of each
+                               candidate of the last frame's pool, pool order
+                               ([C_{n-1} ; frame]); entries [0, last_pool) valid */
+  int32_t count;            /* |C_n| = min(B, frames_seen * T)                   */
+  int32_t capacity;         /* B                                                 */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t last_pool;        /* c_{n-1} + T of the last frame (0 before any)      */
+  int32_t scores_stride;
+  int64_t frames_seen;
+} statekv_state_view;
+
+/* View of the detailed cache D_n (borrowed, same validity as above). */
+typedef struct statekv_cache_view {
+  const void* k;      /* device, [Hkv][capacity][d] bf16                         */
+  const void* v;      /* device, [Hkv][capacity][d] bf16                         */
+  int64_t length;     /* tokens held: min(frames_seen*T, capacity)               */
+  int64_t capacity;   /* detailed_capacity                                      */
+  int64_t start;      /* original position of the oldest token held; with
+                         D_RING it lives in slot (start-position_offset) mod cap */
+  int32_t n_kv_heads;
+  int32_t head_dim;
+} statekv_cache_view;
+
+/* Bytes of device workspace a layer with this configuration needs.
+ * Host only; returns STATEKV_ERR_INVALID_ARGUMENT / _UNSUPPORTED for bad
+ * configurations. */
+int statekv_workspace_bytes(const statekv_layer_config* cfg, size_t* bytes);
+
+/* Create a layer over a caller-allocated device workspace of at least
+ * statekv_workspace_bytes() bytes, 256-byte aligned, kept alive until
+ * statekv_free_layer.  Host only (enqueues nothing): the layer starts with an
+ * empty compressed state and an empty detailed cache. */
+int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace,
+                       size_t workspace_bytes, statekv_layer** out);
+
+/* The per-frame StateKV step (the four parts listed at the top) for the next
+ * frame n = frames_seen: reads q/k/v, writes o, updates C and D, and advances
+ * frames_seen.  Kernels: attention statistics pass, attention output + score
+ * pass, split reduction, top-B select, gather + detailed-cache append. */
+int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
+                          const void* v, float* o, void* stream);
+
+/* Quadratic baseline on the same layer object (full causal self-attention, the
+ * pages' "Full SA"): appends the frame to D, then the frame's queries attend
+ * over D[0 : (n+1)T] causally; C is never touched.  A layer serves either this
+ * or statekv_prefill_frame, not both (mixing returns INVALID_ARGUMENT).  Needs
+ * a linear (non-ring) D. */
+int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void* k,
+                                 const void* v, float* o, void* stream);
+
+/* Views (host only). */
+int statekv_state(const statekv_layer* layer, statekv_state_view* out);
+int statekv_detailed_cache(const statekv_layer* layer, statekv_cache_view* out);
+
+/* Forget every frame (host only): empty C and D, frames_seen = 0. */
+int statekv_reset_layer(statekv_layer* layer);
+
+/* Release the host handle (the workspace stays the caller's). */
+int statekv_free_layer(statekv_layer* layer);
+
+/* Human-readable name of a status code (static storage). */
+const char* statekv_status_string(int status);
+
+/* Kernels of statekv_prefill_frame, for the timing hooks below. */
+enum {
+  STATEKV_KERNEL_ATTN_STATS = 0, /* attention pass 1: row statistics           */
+  STATEKV_KERNEL_ATTN_OUT = 1,   /* attention pass 2: O, importance partials   */
+  STATEKV_KERNEL_SPLIT_SUM = 2,  /* fixed-order sum of split O partials        */
+  STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select             */
+  STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append         */
+  STATEKV_NUM_KERNELS = 5
+};
+
+/* Timing hooks for benchmarks (measurement only; results are unaffected).
+ * statekv_profile_start: from now on every statekv_prefill_frame (and
+ * statekv_full_attention_frame: its attention kernel counts as ATTN_OUT, its
+ * split combine as SPLIT_SUM, its append as GATHER) records a
+ * HIP event on its stream immediately before and after each kernel whose bit
+ * is set in kernel_mask (1u << STATEKV_KERNEL_*), for at most max_records
+ * kernel launches (further launches are not recorded).  The events are
+ * created here, on the current device.
+ * statekv_profile_stop: waits for the recorded events, writes per kernel the
+ * summed event-to-event milliseconds (total_ms[STATEKV_NUM_KERNELS]) and the
+ * number of recorded launches (launches[STATEKV_NUM_KERNELS]), stops
+ * recording and destroys the events.  Either output may be NULL. */
+int statekv_profile_start(statekv_layer* layer, uint32_t kernel_mask, int32_t max_records);
+int statekv_profile_stop(statekv_layer* layer, double* total_ms, int64_t* launches);
+
+/* The top-B select used inside the step, exposed for bit-exact testing: of the
+ * n fp32 scores (device, non-negative or +0; NaN ranks lowest), keep
+ * min(budget, n) indices -- larger score first, ties to the lower index -- and
+ * write them in ascending index order to d_out_idx (device, >= min(budget,n)
+ * int32).  1 <= n <= 32768, budget >= 1. */
+int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget,
+                        int32_t* d_out_idx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STATEKV_H_ */

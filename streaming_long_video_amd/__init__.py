@@ -1,0 +1,32 @@
+"""StateKV streaming video prefill on MI355X (gfx950).
+
+The compute path is libstatekv.so: hand-written HIP kernels behind a C ABI
+(include/statekv.h).  This package holds the ctypes binding with the same
+entry-point names (``_binding``), a torch-facing ``Layer`` wrapper and the
+build script.  Importing it loads the library and fails if it is missing.
+"""
+
+from ._binding import (  # noqa: F401
+    STATEKV_FLAG_D_RING,
+    STATEKV_FLAG_NONCAUSAL_FRAME,
+    STATEKV_FLAG_SELECT_SHARED,
+    STATEKV_KERNELS,
+    StateKVError,
+    load_library,
+    make_config,
+    statekv_detailed_cache,
+    statekv_free_layer,
+    statekv_full_attention_frame,
+    statekv_init_layer,
+    statekv_prefill_frame,
+    statekv_profile_start,
+    statekv_profile_stop,
+    statekv_reset_layer,
+    statekv_select_topb,
+    statekv_state,
+    statekv_status_string,
+    statekv_workspace_bytes,
+)
+from .layer import Layer, select_topb  # noqa: F401
+
+load_library()

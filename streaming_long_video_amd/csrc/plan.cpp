@@ -1,0 +1,99 @@
+// Host-side layer plan (see plan.h).
+#include "plan.h"
+
+#include <math.h>
+
+namespace skv {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+int make_plan(const statekv_layer_config* cfg, Plan* p) {
+  if (!cfg || !p) return STATEKV_ERR_INVALID_ARGUMENT;
+  const int32_t Hq = cfg->n_q_heads, Hkv = cfg->n_kv_heads, D = cfg->head_dim;
+  const int32_t T = cfg->frame_tokens, B = cfg->state_budget;
+  if (Hq <= 0 || Hkv <= 0 || T <= 0 || B <= 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (Hq % Hkv) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (cfg->detailed_capacity < T) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (cfg->position_offset < 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (cfg->num_splits < 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (cfg->flags & ~(uint32_t)(STATEKV_FLAG_SELECT_SHARED | STATEKV_FLAG_D_RING |
+                               STATEKV_FLAG_NONCAUSAL_FRAME))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  if (D != 64 && D != 128) return STATEKV_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return STATEKV_ERR_UNSUPPORTED;
+  if (T > 4096) return STATEKV_ERR_UNSUPPORTED;
+  if ((int64_t)B + T > kMaxPool) return STATEKV_ERR_UNSUPPORTED;
+  if (cfg->flags & STATEKV_FLAG_SELECT_SHARED) return STATEKV_ERR_UNSUPPORTED;
+  if (cfg->detailed_capacity > ((int64_t)1 << 40)) return STATEKV_ERR_UNSUPPORTED;
+  if (!(cfg->softmax_scale == cfg->softmax_scale) || isinf(cfg->softmax_scale))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+
+  Plan q = {};
+  q.Hq = Hq;
+  q.Hkv = Hkv;
+  q.G = Hq / Hkv;
+  q.D = D;
+  q.T = T;
+  q.B = B;
+  q.cap = cfg->detailed_capacity;
+  q.offset = cfg->position_offset;
+  q.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(1.0 / sqrt((double)D));
+  q.flags = cfg->flags;
+  q.ntblk = ceil_div(T, kTokBlk);
+  q.nqblk = q.G * q.ntblk;
+  q.rt = ceil_div(q.nqblk, kRowBlk);
+  q.tpad = q.ntblk * kTokBlk;
+  q.max_pool = B + T;
+  q.max_tiles = ceil_div(q.max_pool, kKeyTile);
+  const int per_split = Hkv * q.rt;
+  int s = cfg->num_splits;
+  if (s == 0) s = per_split >= kTargetWGs ? 1 : kTargetWGs / per_split;
+  if (s > q.max_tiles) s = q.max_tiles;
+  if (s < 1) s = 1;
+  q.splits = s;
+  q.ldsig = ceil_div(q.max_pool, kKeyTile) * kKeyTile;
+  // full-attention baseline: the pool grows to the whole detailed cache
+  int64_t full_tiles = (q.cap + kKeyTile - 1) / kKeyTile;
+  int fs = cfg->num_splits ? cfg->num_splits
+                           : (per_split >= 2 * kTargetWGs ? 1 : 2 * kTargetWGs / per_split);
+  if (fs > kMaxFullSplits) fs = kMaxFullSplits;
+  if (fs > full_tiles) fs = (int)full_tiles;
+  if (fs < 1) fs = 1;
+  q.full_splits = fs;
+  q.part_splits = q.splits > q.full_splits ? q.splits : q.full_splits;
+
+  const size_t A = 256;
+  size_t off = 0;
+  const size_t c_rows = (size_t)Hkv * B;
+  const size_t d_rows = (size_t)Hkv * (size_t)q.cap;
+  for (int i = 0; i < 2; ++i) {
+    q.off_ck[i] = off; off = align_up(off + c_rows * D * 2, A);
+    q.off_cv[i] = off; off = align_up(off + c_rows * D * 2, A);
+    q.off_cpos[i] = off; off = align_up(off + c_rows * 8, A);
+  }
+  q.off_dk = off; off = align_up(off + d_rows * D * 2, A);
+  q.off_dv = off; off = align_up(off + d_rows * D * 2, A);
+  const size_t stat = (size_t)q.part_splits * Hq * q.tpad * 4;
+  q.off_m = off; off = align_up(off + stat, A);
+  q.off_l = off; off = align_up(off + stat, A);
+  q.off_o = off; off = align_up(off + (size_t)q.part_splits * T * Hq * D * 4, A);
+  q.off_sig = off; off = align_up(off + (size_t)Hkv * q.rt * q.ldsig * 4, A);
+  q.off_scores = off; off = align_up(off + (size_t)Hkv * q.ldsig * 4, A);
+  q.off_sel = off; off = align_up(off + (size_t)Hkv * B * 4, A);
+  q.total = off;
+  *p = q;
+  return STATEKV_OK;
+}
+
+int splits_for_pool(const Plan& p, int pool) {
+  int tiles = ceil_div(pool, kKeyTile);
+  return p.splits < tiles ? p.splits : tiles;
+}
+
+}  // namespace skv

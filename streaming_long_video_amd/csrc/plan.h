@@ -1,0 +1,54 @@
+// Host-side layer plan: configuration checks, derived sizes and the carve-up
+// of the caller's device workspace.  Plain C++ (no HIP), so it is also built
+// and tested with the host compiler alone.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "statekv.h"
+
+namespace skv {
+
+// Kernel tiling shared by the host plan and the kernels.
+constexpr int kTokBlk = 32;     // query tokens per MFMA block (MFMA n dimension)
+constexpr int kWaves = 4;       // waves per attention workgroup
+constexpr int kQBlkPerWave = 2; // query blocks held by each wave
+constexpr int kRowBlk = kWaves * kQBlkPerWave;  // query blocks per row tile
+constexpr int kKeyTile = 64;    // keys staged in LDS per step
+constexpr int kTargetWGs = 256; // one workgroup per compute unit on MI355X
+constexpr int kMaxPool = 32768; // B + T limit (select keeps the pool in LDS)
+constexpr int kMaxFullSplits = 64;
+
+struct Plan {
+  // configuration
+  int32_t Hq, Hkv, G, D, T, B;
+  int64_t cap, offset;
+  float scale;        // softmax scale applied to the logits
+  uint32_t flags;
+  // attention grid
+  int32_t ntblk;      // ceil(T / kTokBlk): token blocks per query head
+  int32_t nqblk;      // G * ntblk: query blocks per KV head
+  int32_t rt;         // row tiles per KV head = ceil(nqblk / kRowBlk)
+  int32_t tpad;       // ntblk * kTokBlk
+  int32_t max_pool;   // B + T
+  int32_t max_tiles;  // ceil(max_pool / kKeyTile)
+  int32_t splits;     // key splits of the StateKV attention grid
+  int32_t ldsig;      // row stride (floats) of score partials / scores
+  int32_t full_splits;  // key splits of the full-attention baseline
+  int32_t part_splits;  // max(splits, full_splits): partial buffers sized for it
+  // workspace offsets (bytes, 256-aligned)
+  size_t off_ck[2], off_cv[2], off_cpos[2];
+  size_t off_dk, off_dv;
+  size_t off_m, off_l, off_o;
+  size_t off_sig, off_scores, off_sel;
+  size_t total;
+};
+
+// Fills *plan from *cfg.  Returns STATEKV_OK or an error status.
+int make_plan(const statekv_layer_config* cfg, Plan* plan);
+
+// Splits actually used for a pool of `pool` candidates (never more than tiles).
+int splits_for_pool(const Plan& p, int pool);
+
+}  // namespace skv

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace skv {
+
+// Arguments of the two attention passes over the pool [C_{n-1} ; frame].
+struct AttnArgs {
+  const uint16_t* q;   // [T][Hq][D] bf16
+  const uint16_t* kf;  // [T][Hkv][D] bf16, frame keys
+  const uint16_t* vf;  // [T][Hkv][D] bf16, frame values
+  const uint16_t* kc;  // [Hkv][ldc][D] bf16, state keys (rows [0, c) live)
+  const uint16_t* vc;  // [Hkv][ldc][D] bf16, state values
+  float* m_part;       // [S][Hq][tpad] per-split row max of raw logits
+  float* l_part;       // [S][Hq][tpad] per-split sum of exp relative to m
+  float* o_out;        // [T][Hq][D] fp32 when S == 1, else [S][T][Hq][D] partials
+  float* sig_part;     // [Hkv][rt][ldsig] per-row-tile score partials
+  int64_t ldc;         // state rows per KV head (B)
+  int T, Hq, Hkv, G;
+  int c;               // live state rows; pool = c + T
+  int ntblk, nqblk, rt, tpad;
+  int S;               // key splits
+  int ldsig;
+  float scale_log2;    // softmax scale * log2(e)
+  int causal;
+};
+
+hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st);
+// o[i] = sum_{s<S} part[s*n + i] (fixed order); n counts floats.
+hipError_t launch_split_sum(const float* part, int S, int64_t n, float* o, hipStream_t st);
+
+// Sums score partials, writes scores, selects the top-B (or keeps all).
+// Standalone mode: rt = 1 and sig_part holds the scores (scores may be null).
+hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
+                         int budget, float* scores, int ldscores, int32_t* sel,
+                         int ldsel, hipStream_t st);
+
+struct GatherArgs {
+  const uint16_t* kc_prev;  // [Hkv][B][D]
+  const uint16_t* vc_prev;
+  const int64_t* pos_prev;  // [Hkv][B]
+  const uint16_t* kf;       // [T][Hkv][D]
+  const uint16_t* vf;
+  const int32_t* sel;       // [Hkv][B] pool indices, ascending (ignored if keep_all)
+  uint16_t* kc_next;
+  uint16_t* vc_next;
+  int64_t* pos_next;
+  uint16_t* kd;             // [Hkv][cap][D] detailed cache (null: no append)
+  uint16_t* vd;
+  int64_t cap;
+  int64_t frame_base;       // n*T: frame index of token 0 (relative to the offset)
+  int64_t pos_offset;
+  int B, T, Hkv, c, newc;
+  int keep_all;             // pool <= B: C_n = [C_{n-1} ; frame]
+  int ring;
+};
+hipError_t launch_gather_append(const GatherArgs& g, int D, hipStream_t st);
+hipError_t launch_append_only(const GatherArgs& g, int D, hipStream_t st);
+
+// Full-attention baseline (single online-softmax pass): the pool is
+// [D[0:c) ; frame], causal within the frame.  With S == 1 it writes the
+// normalised O to o_out; otherwise unnormalised partials plus (m, l).
+hipError_t launch_full_attn(const AttnArgs& a, int D, hipStream_t st);
+// Combines the unnormalised split partials of the full-attention baseline.
+hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, hipStream_t st);
+
+}  // namespace skv

@@ -1,0 +1,377 @@
+// C ABI of the StateKV streaming video-prefill library (declared in statekv.h).
+//
+// Host side of the per-frame step: argument checks, the workspace carve-up
+// (plan.cpp), the launch sequence on the caller's stream, and the host mirror
+// of the layer's progress (frames seen, live state size, detailed-cache
+// length, which compressed-state buffer is current).  Every quantity the
+// launches need is known on the host ahead of time, so nothing is read back
+// from the device.
+#include <math.h>
+
+#include <new>
+#include <vector>
+
+#include "plan.h"
+#include "skv_internal.h"
+
+// Timing hook state: one (kernel, before, after) event triple per recorded launch.
+struct ProfRecord {
+  int kernel;
+  hipEvent_t before, after;
+};
+
+struct statekv_layer {
+  skv::Plan plan;
+  char* ws;          // device workspace base
+  int64_t n;         // frames seen
+  int32_t c;         // live compressed-state rows
+  int32_t cur;       // index (0/1) of the buffer holding C_n
+  int32_t last_pool; // pool size of the last frame
+  int32_t mode;      // 0 unused, 1 StateKV, 2 full attention
+  // timing hooks
+  uint32_t prof_mask;
+  std::vector<ProfRecord> prof;  // pre-created events
+  size_t prof_used;
+};
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <class T>
+T* at(const statekv_layer* L, size_t off) {
+  return reinterpret_cast<T*>(L->ws + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? STATEKV_OK : STATEKV_ERR_HIP; }
+
+skv::AttnArgs attn_args(const statekv_layer* L, const void* q, const void* k, const void* v) {
+  const skv::Plan& p = L->plan;
+  skv::AttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kf = static_cast<const uint16_t*>(k);
+  a.vf = static_cast<const uint16_t*>(v);
+  a.m_part = at<float>(L, p.off_m);
+  a.l_part = at<float>(L, p.off_l);
+  a.sig_part = at<float>(L, p.off_sig);
+  a.T = p.T;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
+  a.ntblk = p.ntblk;
+  a.nqblk = p.nqblk;
+  a.rt = p.rt;
+  a.tpad = p.tpad;
+  a.ldsig = p.ldsig;
+  a.scale_log2 = p.scale * kLog2e;
+  a.causal = (p.flags & STATEKV_FLAG_NONCAUSAL_FRAME) ? 0 : 1;
+  return a;
+}
+
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+// Runs one kernel launch, bracketed by timing events when the hook asks for it.
+template <class F>
+hipError_t timed(statekv_layer* L, int kernel, hipStream_t st, F&& launch) {
+  ProfRecord* r = nullptr;
+  if ((L->prof_mask >> kernel) & 1u && L->prof_used < L->prof.size()) {
+    r = &L->prof[L->prof_used++];
+    r->kernel = kernel;
+    hipError_t e = hipEventRecord(r->before, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (r && e == hipSuccess) e = hipEventRecord(r->after, st);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int statekv_workspace_bytes(const statekv_layer_config* cfg, size_t* bytes) {
+  if (!bytes) return STATEKV_ERR_INVALID_ARGUMENT;
+  skv::Plan p;
+  const int st = skv::make_plan(cfg, &p);
+  if (st != STATEKV_OK) return st;
+  *bytes = p.total;
+  return STATEKV_OK;
+}
+
+int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace, size_t workspace_bytes,
+                       statekv_layer** out) {
+  if (!out || !d_workspace) return STATEKV_ERR_INVALID_ARGUMENT;
+  skv::Plan p;
+  const int st = skv::make_plan(cfg, &p);
+  if (st != STATEKV_OK) return st;
+  if (workspace_bytes < p.total) return STATEKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(d_workspace) & 255u) return STATEKV_ERR_WORKSPACE;
+  statekv_layer* L = new (std::nothrow) statekv_layer();
+  if (!L) return STATEKV_ERR_INVALID_ARGUMENT;
+  L->plan = p;
+  L->ws = static_cast<char*>(d_workspace);
+  L->n = 0;
+  L->c = 0;
+  L->cur = 0;
+  L->last_pool = 0;
+  L->mode = 0;
+  L->prof_mask = 0;
+  L->prof_used = 0;
+  *out = L;
+  return STATEKV_OK;
+}
+
+int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const void* v, float* o,
+                          void* stream) {
+  if (!L || !q || !k || !v || !o) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  if (L->mode == 2) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  const bool ring = p.flags & STATEKV_FLAG_D_RING;
+  const int64_t next_len = (L->n + 1) * (int64_t)p.T;
+  if (!ring && next_len > p.cap) return STATEKV_ERR_CAPACITY;
+  if (L->n * (int64_t)p.T + p.T + p.offset > ((int64_t)1 << 62)) return STATEKV_ERR_CAPACITY;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  L->mode = 1;
+
+  const int cur = L->cur, nxt = cur ^ 1;
+  const int c = L->c;
+  const int pool = c + p.T;
+  const int newc = pool < p.B ? pool : p.B;
+
+  skv::AttnArgs a = attn_args(L, q, k, v);
+  a.kc = at<uint16_t>(L, p.off_ck[cur]);
+  a.vc = at<uint16_t>(L, p.off_cv[cur]);
+  a.ldc = p.B;
+  a.c = c;
+  a.S = skv::splits_for_pool(p, pool);
+  float* opart = at<float>(L, p.off_o);
+  a.o_out = a.S == 1 ? o : opart;
+
+  hipError_t e = timed(L, STATEKV_KERNEL_ATTN_STATS, st,
+                       [&] { return skv::launch_attn_stats(a, p.D, st); });
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_attn_out(a, p.D, st); });
+  if (e == hipSuccess && a.S > 1)
+    e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st, [&] {
+      return skv::launch_split_sum(opart, a.S, (int64_t)p.T * p.Hq * p.D, o, st);
+    });
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_SELECT, st, [&] {
+      return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
+                                at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
+                                p.B, st);
+    });
+  if (e == hipSuccess) {
+    skv::GatherArgs g = {};
+    g.kc_prev = a.kc;
+    g.vc_prev = a.vc;
+    g.pos_prev = at<int64_t>(L, p.off_cpos[cur]);
+    g.kf = a.kf;
+    g.vf = a.vf;
+    g.sel = at<int32_t>(L, p.off_sel);
+    g.kc_next = at<uint16_t>(L, p.off_ck[nxt]);
+    g.vc_next = at<uint16_t>(L, p.off_cv[nxt]);
+    g.pos_next = at<int64_t>(L, p.off_cpos[nxt]);
+    g.kd = at<uint16_t>(L, p.off_dk);
+    g.vd = at<uint16_t>(L, p.off_dv);
+    g.cap = p.cap;
+    g.frame_base = L->n * (int64_t)p.T;
+    g.pos_offset = p.offset;
+    g.B = p.B;
+    g.T = p.T;
+    g.Hkv = p.Hkv;
+    g.c = c;
+    g.newc = newc;
+    g.keep_all = pool <= p.B;
+    g.ring = ring;
+    e = timed(L, STATEKV_KERNEL_GATHER, st, [&] { return skv::launch_gather_append(g, p.D, st); });
+  }
+  if (e != hipSuccess) return hip_status(e);
+  L->cur = nxt;
+  L->c = newc;
+  L->last_pool = pool;
+  L->n += 1;
+  return STATEKV_OK;
+}
+
+int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k, const void* v,
+                                 float* o, void* stream) {
+  if (!L || !q || !k || !v || !o) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  if (L->mode == 1) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  if (p.flags & STATEKV_FLAG_D_RING) return STATEKV_ERR_UNSUPPORTED;
+  const int64_t hist = L->n * (int64_t)p.T;
+  if (hist + p.T > p.cap) return STATEKV_ERR_CAPACITY;
+  if (hist + p.T > (int64_t)0x7FFFFFFF) return STATEKV_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  L->mode = 2;
+
+  skv::GatherArgs g = {};
+  g.kf = static_cast<const uint16_t*>(k);
+  g.vf = static_cast<const uint16_t*>(v);
+  g.kd = at<uint16_t>(L, p.off_dk);
+  g.vd = at<uint16_t>(L, p.off_dv);
+  g.cap = p.cap;
+  g.frame_base = hist;
+  g.pos_offset = p.offset;
+  g.B = p.B;
+  g.T = p.T;
+  g.Hkv = p.Hkv;
+  hipError_t e =
+      timed(L, STATEKV_KERNEL_GATHER, st, [&] { return skv::launch_append_only(g, p.D, st); });
+
+  skv::AttnArgs a = attn_args(L, q, k, v);
+  a.kc = at<uint16_t>(L, p.off_dk);
+  a.vc = at<uint16_t>(L, p.off_dv);
+  a.ldc = p.cap;
+  a.c = (int)hist;
+  const int tiles = (int)((hist + p.T + skv::kKeyTile - 1) / skv::kKeyTile);
+  a.S = p.full_splits < tiles ? p.full_splits : tiles;
+  a.o_out = a.S == 1 ? o : at<float>(L, p.off_o);
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_full_attn(a, p.D, st); });
+  if (e == hipSuccess && a.S > 1)
+    e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st,
+              [&] { return skv::launch_full_combine(a, o, p.D, st); });
+  if (e != hipSuccess) return hip_status(e);
+  L->n += 1;
+  return STATEKV_OK;
+}
+
+int statekv_state(const statekv_layer* L, statekv_state_view* out) {
+  if (!L || !out) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  statekv_state_view v = {};
+  v.k = at<uint16_t>(L, p.off_ck[L->cur]);
+  v.v = at<uint16_t>(L, p.off_cv[L->cur]);
+  v.pos = at<int64_t>(L, p.off_cpos[L->cur]);
+  v.last_scores = at<float>(L, p.off_scores);
+  v.count = L->c;
+  v.capacity = p.B;
+  v.n_kv_heads = p.Hkv;
+  v.head_dim = p.D;
+  v.last_pool = L->mode == 1 ? L->last_pool : 0;
+  v.scores_stride = p.ldsig;
+  v.frames_seen = L->n;
+  *out = v;
+  return STATEKV_OK;
+}
+
+int statekv_detailed_cache(const statekv_layer* L, statekv_cache_view* out) {
+  if (!L || !out) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  statekv_cache_view v = {};
+  v.k = at<uint16_t>(L, p.off_dk);
+  v.v = at<uint16_t>(L, p.off_dv);
+  const int64_t total = L->n * (int64_t)p.T;
+  v.length = total < p.cap ? total : p.cap;
+  v.capacity = p.cap;
+  v.start = p.offset + (total > p.cap ? total - p.cap : 0);
+  v.n_kv_heads = p.Hkv;
+  v.head_dim = p.D;
+  *out = v;
+  return STATEKV_OK;
+}
+
+int statekv_reset_layer(statekv_layer* L) {
+  if (!L) return STATEKV_ERR_INVALID_ARGUMENT;
+  L->n = 0;
+  L->c = 0;
+  L->cur = 0;
+  L->last_pool = 0;
+  L->mode = 0;
+  return STATEKV_OK;
+}
+
+namespace {
+void destroy_profile_events(statekv_layer* L) {
+  for (ProfRecord& r : L->prof) {
+    hipEventDestroy(r.before);
+    hipEventDestroy(r.after);
+  }
+  L->prof.clear();
+  L->prof_used = 0;
+  L->prof_mask = 0;
+}
+}  // namespace
+
+int statekv_profile_start(statekv_layer* L, uint32_t kernel_mask, int32_t max_records) {
+  if (!L || max_records < 0 || (kernel_mask >> STATEKV_NUM_KERNELS))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  destroy_profile_events(L);
+  L->prof.reserve((size_t)max_records);
+  for (int32_t i = 0; i < max_records; ++i) {
+    ProfRecord r = {0, nullptr, nullptr};
+    if (hipEventCreate(&r.before) != hipSuccess) {
+      destroy_profile_events(L);
+      return STATEKV_ERR_HIP;
+    }
+    if (hipEventCreate(&r.after) != hipSuccess) {
+      hipEventDestroy(r.before);
+      destroy_profile_events(L);
+      return STATEKV_ERR_HIP;
+    }
+    L->prof.push_back(r);
+  }
+  L->prof_mask = kernel_mask;
+  return STATEKV_OK;
+}
+
+int statekv_profile_stop(statekv_layer* L, double* total_ms, int64_t* launches) {
+  if (!L) return STATEKV_ERR_INVALID_ARGUMENT;
+  double ms[STATEKV_NUM_KERNELS] = {0};
+  int64_t cnt[STATEKV_NUM_KERNELS] = {0};
+  int status = STATEKV_OK;
+  for (size_t i = 0; i < L->prof_used; ++i) {
+    const ProfRecord& r = L->prof[i];
+    float t = 0.f;
+    if (hipEventSynchronize(r.after) != hipSuccess ||
+        hipEventElapsedTime(&t, r.before, r.after) != hipSuccess) {
+      status = STATEKV_ERR_HIP;
+      break;
+    }
+    ms[r.kernel] += t;
+    cnt[r.kernel] += 1;
+  }
+  destroy_profile_events(L);
+  for (int k = 0; k < STATEKV_NUM_KERNELS; ++k) {
+    if (total_ms) total_ms[k] = ms[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return status;
+}
+
+int statekv_free_layer(statekv_layer* L) {
+  if (!L) return STATEKV_ERR_INVALID_ARGUMENT;
+  destroy_profile_events(L);
+  delete L;
+  return STATEKV_OK;
+}
+
+const char* statekv_status_string(int status) {
+  switch (status) {
+    case STATEKV_OK: return "ok";
+    case STATEKV_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case STATEKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case STATEKV_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case STATEKV_ERR_CAPACITY: return "detailed cache capacity exceeded";
+    case STATEKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_t* d_out_idx,
+                        void* stream) {
+  if (!d_scores || !d_out_idx) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (n < 1 || budget < 1) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
+                                       budget, st));
+}
+
+}  // extern "C"

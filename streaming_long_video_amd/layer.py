@@ -1,0 +1,130 @@
+"""Torch-facing wrapper of one StateKV layer.
+
+torch supplies device memory (the workspace and the frame tensors) and the
+HIP stream; the computation is entirely the library's.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream]) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class Layer:
+    """One transformer layer's StateKV caches on the current GPU.
+
+    q: [T][Hq][d] bf16, k/v: [T][Hkv][d] bf16 (RoPE already applied at the
+    tokens' original positions), output: [T][Hq][d] float32.
+    """
+
+    def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, frame_tokens: int,
+                 state_budget: int, detailed_capacity: int, position_offset: int = 0,
+                 softmax_scale: float = 0.0, flags: int = 0, num_splits: int = 0,
+                 device: Optional[torch.device] = None):
+        self.cfg = B.make_config(n_q_heads, n_kv_heads, head_dim, frame_tokens, state_budget,
+                                 detailed_capacity, position_offset, softmax_scale, flags,
+                                 num_splits)
+        self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
+        self.T, self.B = frame_tokens, state_budget
+        self.capacity = detailed_capacity
+        nbytes = B.statekv_workspace_bytes(self.cfg)
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.handle = B.statekv_init_layer(self.cfg, self.workspace.data_ptr(), nbytes)
+        self.workspace_bytes = nbytes
+
+    # -- per-frame calls -------------------------------------------------------
+    def _check_frame(self, q, k, v, out):
+        T, Hq, Hkv, d = self.T, self.Hq, self.Hkv, self.d
+        for name, x, shape in (("q", q, (T, Hq, d)), ("k", k, (T, Hkv, d)),
+                               ("v", v, (T, Hkv, d))):
+            if x.dtype != torch.bfloat16 or tuple(x.shape) != shape or not x.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {shape}")
+            if x.device != self.workspace.device:
+                raise ValueError(f"{name} is not on the layer's device")
+        if out is None:
+            out = torch.empty((T, Hq, d), dtype=torch.float32, device=self.workspace.device)
+        elif (out.dtype != torch.float32 or tuple(out.shape) != (T, Hq, d)
+              or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous float32 tensor of shape (T, Hq, d)")
+        return out
+
+    def prefill(self, q, k, v, out=None, stream=None):
+        """StateKV step for the next frame; returns the attention output."""
+        out = self._check_frame(q, k, v, out)
+        B.statekv_prefill_frame(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), _stream_ptr(stream))
+        return out
+
+    def full_attention(self, q, k, v, out=None, stream=None):
+        """Quadratic baseline: append the frame to D, attend over all of D."""
+        out = self._check_frame(q, k, v, out)
+        B.statekv_full_attention_frame(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                       out.data_ptr(), _stream_ptr(stream))
+        return out
+
+    # -- views -----------------------------------------------------------------
+    def _ws_slice(self, ptr: int, nbytes: int, dtype, shape):
+        off = ptr - self.workspace.data_ptr()
+        assert 0 <= off and off + nbytes <= self.workspace_bytes
+        return self.workspace[off:off + nbytes].view(dtype).view(shape)
+
+    def state(self):
+        """C_n as workspace views: dict(k, v, pos, count, scores, pool, frames_seen)."""
+        v = B.statekv_state(self.handle)
+        Hkv, Bc, d = v.n_kv_heads, v.capacity, v.head_dim
+        rows = Hkv * Bc * d * 2
+        return {
+            "k": self._ws_slice(v.k, rows, torch.bfloat16, (Hkv, Bc, d)),
+            "v": self._ws_slice(v.v, rows, torch.bfloat16, (Hkv, Bc, d)),
+            "pos": self._ws_slice(v.pos, Hkv * Bc * 8, torch.int64, (Hkv, Bc)),
+            "scores": self._ws_slice(v.last_scores, Hkv * v.scores_stride * 4, torch.float32,
+                                     (Hkv, v.scores_stride)),
+            "count": v.count,
+            "pool": v.last_pool,
+            "frames_seen": v.frames_seen,
+        }
+
+    def detailed_cache(self):
+        """D_n as workspace views: dict(k, v, length, start)."""
+        v = B.statekv_detailed_cache(self.handle)
+        Hkv, cap, d = v.n_kv_heads, v.capacity, v.head_dim
+        rows = Hkv * cap * d * 2
+        return {
+            "k": self._ws_slice(v.k, rows, torch.bfloat16, (Hkv, cap, d)),
+            "v": self._ws_slice(v.v, rows, torch.bfloat16, (Hkv, cap, d)),
+            "length": v.length,
+            "start": v.start,
+        }
+
+    def reset(self):
+        B.statekv_reset_layer(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            B.statekv_free_layer(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def select_topb(scores: torch.Tensor, budget: int, stream=None) -> torch.Tensor:
+    """The library's top-B select on a float32 device vector (ascending indices)."""
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous 1-D float32 tensor")
+    n = scores.shape[0]
+    out = torch.empty(min(n, budget), dtype=torch.int32, device=scores.device)
+    B.statekv_select_topb(scores.data_ptr(), n, budget, out.data_ptr(), _stream_ptr(stream))
+    return out

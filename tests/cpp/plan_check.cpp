@@ -1,0 +1,99 @@
+// Host-only checks of the layer plan (built with g++ and sanitizers, no HIP):
+// regions are 256-byte aligned, disjoint and inside the total; sizes follow
+// the configuration; invalid configurations are rejected.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <utility>
+#include <vector>
+
+#include "plan.h"
+
+static int failures = 0;
+#define CHECK(x)                                                  \
+  do {                                                            \
+    if (!(x)) {                                                   \
+      fprintf(stderr, "%s:%d: CHECK failed: %s\n", __FILE__, __LINE__, #x); \
+      ++failures;                                                 \
+    }                                                             \
+  } while (0)
+
+static statekv_layer_config cfg(int hq, int hkv, int d, int t, int b, long long cap) {
+  statekv_layer_config c = {};
+  c.n_q_heads = hq;
+  c.n_kv_heads = hkv;
+  c.head_dim = d;
+  c.frame_tokens = t;
+  c.state_budget = b;
+  c.detailed_capacity = cap;
+  return c;
+}
+
+static void check_layout(const statekv_layer_config& c) {
+  skv::Plan p;
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK);
+  const size_t cr = (size_t)p.Hkv * p.B, dr = (size_t)p.Hkv * p.cap;
+  std::vector<std::pair<size_t, size_t>> r = {
+      {p.off_ck[0], cr * p.D * 2}, {p.off_cv[0], cr * p.D * 2}, {p.off_cpos[0], cr * 8},
+      {p.off_ck[1], cr * p.D * 2}, {p.off_cv[1], cr * p.D * 2}, {p.off_cpos[1], cr * 8},
+      {p.off_dk, dr * p.D * 2},     {p.off_dv, dr * p.D * 2},
+      {p.off_m, (size_t)p.part_splits * p.Hq * p.tpad * 4},
+      {p.off_l, (size_t)p.part_splits * p.Hq * p.tpad * 4},
+      {p.off_o, (size_t)p.part_splits * p.T * p.Hq * p.D * 4},
+      {p.off_sig, (size_t)p.Hkv * p.rt * p.ldsig * 4},
+      {p.off_scores, (size_t)p.Hkv * p.ldsig * 4},
+      {p.off_sel, (size_t)p.Hkv * p.B * 4}};
+  std::sort(r.begin(), r.end());
+  for (size_t i = 0; i < r.size(); ++i) {
+    CHECK(r[i].first % 256 == 0);
+    CHECK(r[i].first + r[i].second <= p.total);
+    if (i + 1 < r.size()) CHECK(r[i].first + r[i].second <= r[i + 1].first);
+  }
+  CHECK(p.G * p.Hkv == p.Hq);
+  CHECK(p.ntblk * skv::kTokBlk >= p.T && (p.ntblk - 1) * skv::kTokBlk < p.T);
+  CHECK(p.rt * skv::kRowBlk >= p.nqblk);
+  CHECK(p.ldsig >= p.B + p.T && p.ldsig % skv::kKeyTile == 0);
+  CHECK(p.splits >= 1 && p.splits <= p.max_tiles);
+  CHECK(p.Hkv * p.rt * p.splits <= skv::kTargetWGs || p.splits == 1);
+  for (int pool = 1; pool <= p.B + p.T; pool += 97) {
+    const int s = skv::splits_for_pool(p, pool);
+    CHECK(s >= 1 && s <= (pool + skv::kKeyTile - 1) / skv::kKeyTile);
+  }
+}
+
+int main() {
+  check_layout(cfg(28, 4, 128, 256, 4096, 131072));
+  check_layout(cfg(14, 2, 64, 256, 1024, 16384));
+  check_layout(cfg(12, 2, 128, 256, 2048, 65536));
+  check_layout(cfg(2, 1, 64, 16, 32, 128));
+  check_layout(cfg(6, 2, 128, 17, 50, 102));
+  check_layout(cfg(16, 1, 64, 4096, 28672, 4096));
+  skv::Plan p;
+  statekv_layer_config c = cfg(28, 4, 128, 256, 4096, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.rt == 7);
+  c = cfg(28, 4, 96, 256, 4096, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  c = cfg(28, 5, 128, 256, 4096, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  c = cfg(28, 4, 128, 256, 4096, 100);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  c = cfg(28, 4, 128, 256, 32600, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  c = cfg(34, 2, 128, 256, 4096, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  c = cfg(28, 4, 128, 0, 4096, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  c = cfg(28, 4, 128, 256, 4096, 131072);
+  c.flags = 1u << 7;
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  c.flags = STATEKV_FLAG_SELECT_SHARED;
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  c.flags = 0;
+  c.num_splits = 3;
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 3);
+  CHECK(skv::make_plan(nullptr, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  if (failures) return 1;
+  printf("plan checks passed\n");
+  return 0;
+}

@@ -1,0 +1,118 @@
+"""Helpers for the GPU parity tests: device copies, views, error metrics, a
+teacher-forced oracle comparison loop."""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+# Acceptance bounds for the attention output (fp32 O against the float64
+# oracle, both fed identical bf16 inputs).
+O_MAXABS = 2e-2
+O_RELRMS = 1e-3
+# fp32 scores against float64 scores
+SCORE_RTOL = 2e-4
+SCORE_ATOL = 2e-5
+# free-running selected-set agreement
+SELECT_AGREEMENT = 0.995
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> contiguous cuda bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def o_errors(o_gpu: np.ndarray, o_ref: np.ndarray):
+    d = o_gpu.astype(np.float64) - o_ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(o_ref))
+
+
+@dataclasses.dataclass
+class StateSnapshot:
+    count: int
+    pos: List[np.ndarray]
+    k: List[np.ndarray]
+    v: List[np.ndarray]
+    scores: List[np.ndarray]
+    pool: int
+
+
+def snapshot(layer) -> StateSnapshot:
+    torch.cuda.synchronize()
+    st = layer.state()
+    c, pool = st["count"], st["pool"]
+    pos = st["pos"][:, :c].cpu().numpy()
+    k = to_bits(st["k"][:, :c])
+    v = to_bits(st["v"][:, :c])
+    sc = st["scores"][:, :pool].cpu().numpy()
+    H = pos.shape[0]
+    return StateSnapshot(c, [pos[h] for h in range(H)], [k[h] for h in range(H)],
+                         [v[h] for h in range(H)], [sc[h] for h in range(H)], pool)
+
+
+@dataclasses.dataclass
+class FrameReport:
+    n: int
+    maxabs: float
+    relrms: float
+    score_err: float
+    kept_match: int
+    kept_total: int
+
+
+def teacher_forced_frame(orc, layer, n, q, k, v, o_gpu_dev=None) -> FrameReport:
+    """Run GPU frame n and the oracle step from the GPU's C_{n-1}; compare."""
+    before = snapshot(layer)
+    orc.load_state(n, before.pos, before.k, before.v)
+    q_d, k_d, v_d = to_dev(q), to_dev(k), to_dev(v)
+    o = layer.prefill(q_d, k_d, v_d, out=o_gpu_dev)
+    after = snapshot(layer)
+    ref = orc.step(q, k, v)
+    maxabs, relrms = o_errors(o.cpu().numpy(), ref.o)
+    score_err = 0.0
+    match = total = 0
+    for h in range(len(ref.scores)):
+        np.testing.assert_array_equal(ref.pool_positions[h].shape[0], after.pool)
+        s_ref = ref.scores[h]
+        s_gpu = after.scores[h].astype(np.float64)
+        score_err = max(score_err, float((np.abs(s_gpu - s_ref) /
+                                          (SCORE_ATOL + SCORE_RTOL * np.abs(s_ref))).max()))
+        kept_ref = set(ref.kept_positions[h].tolist())
+        kept_gpu = after.pos[h].tolist()
+        assert kept_gpu == sorted(kept_gpu), "state positions must ascend"
+        assert len(kept_gpu) == len(kept_ref)
+        match += len(kept_ref.intersection(kept_gpu))
+        total += len(kept_ref)
+    return FrameReport(n, maxabs, relrms, score_err, match, total)
+
+
+def check_caches_bitwise(layer, frames_k, frames_v, n_frames: Optional[int] = None):
+    """Every state row equals the detailed-cache row at its position, and the
+    detailed cache equals the concatenated input frames (bit for bit)."""
+    torch.cuda.synchronize()
+    st = layer.state()
+    dc = layer.detailed_cache()
+    c = st["count"]
+    L = dc["length"]
+    dk = to_bits(dc["k"][:, :L])
+    dv = to_bits(dc["v"][:, :L])
+    K = np.concatenate(frames_k) if isinstance(frames_k, list) else frames_k
+    V = np.concatenate(frames_v) if isinstance(frames_v, list) else frames_v
+    K = K.reshape(-1, *K.shape[-2:])[:L]
+    V = V.reshape(-1, *V.shape[-2:])[:L]
+    np.testing.assert_array_equal(dk, np.transpose(K, (1, 0, 2)))
+    np.testing.assert_array_equal(dv, np.transpose(V, (1, 0, 2)))
+    pos = st["pos"][:, :c].cpu().numpy()
+    ck = to_bits(st["k"][:, :c])
+    cv = to_bits(st["v"][:, :c])
+    for h in range(pos.shape[0]):
+        assert np.all(np.diff(pos[h]) > 0)
+        np.testing.assert_array_equal(ck[h], dk[h][pos[h]])
+        np.testing.assert_array_equal(cv[h], dv[h][pos[h]])

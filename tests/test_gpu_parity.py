@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle."""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import framegen
+from gpu_util import (O_MAXABS, O_RELRMS, SELECT_AGREEMENT, check_caches_bitwise, o_errors,
+                      snapshot, teacher_forced_frame, to_dev)
+from oracle import StateKVOracle, full_causal_attention
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import streaming_long_video_amd as skv  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _layer(spec, **kw):
+    cfg = dict(n_q_heads=spec.n_q_heads, n_kv_heads=spec.n_kv_heads, head_dim=spec.head_dim,
+               frame_tokens=spec.frame_tokens, state_budget=spec.state_budget,
+               detailed_capacity=spec.n_frames * spec.frame_tokens)
+    cfg.update(kw)
+    return skv.Layer(**cfg)
+
+
+def _oracle(spec, **kw):
+    return StateKVOracle(spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.frame_tokens,
+                         spec.state_budget, **kw)
+
+
+def _run_teacher_forced(spec, layer=None, orc_kw=None, frames=None):
+    layer = layer or _layer(spec)
+    orc = _oracle(spec, **(orc_kw or {}))
+    qs, ks, vs = frames if frames is not None else framegen.stacked_frames(spec, workers=8)
+    reports = []
+    for n in range(qs.shape[0]):
+        reports.append(teacher_forced_frame(orc, layer, n, qs[n], ks[n], vs[n]))
+    return layer, reports, (qs, ks, vs)
+
+
+def _assert_reports(reports, exact_select=True):
+    worst = max(reports, key=lambda r: r.relrms)
+    print(f"worst frame {worst.n}: maxabs {worst.maxabs:.3e} relrms {worst.relrms:.3e}; "
+          f"max score err {max(r.score_err for r in reports):.3f} x tol")
+    for r in reports:
+        assert r.maxabs <= O_MAXABS, r
+        assert r.relrms <= O_RELRMS, r
+        assert r.score_err <= 1.0, r
+    match = sum(r.kept_match for r in reports)
+    total = sum(r.kept_total for r in reports)
+    if exact_select:
+        assert match == total, (match, total)
+    assert match >= SELECT_AGREEMENT * total
+
+
+def test_hand_example_on_gpu():
+    """The three-frame example worked by hand, embedded in d=64 with zero padding."""
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    layer = skv.Layer(1, 1, 64, 2, 2, detailed_capacity=6, softmax_scale=math.log(2.0))
+    for fr, exp in zip(ex["frames"], ex["expected"]):
+        pad = lambda x: np.pad(np.array(x, dtype=np.float32)[:, None, :], ((0, 0), (0, 0), (0, 62)))
+        q, k, v = (torch.from_numpy(pad(fr[n])).cuda().to(torch.bfloat16) for n in "qkv")
+        o = layer.prefill(q, k, v).cpu().numpy()[:, 0, :2]
+        o_exp = np.array([[float(Fraction(x)) for x in row] for row in exp["o"]])
+        np.testing.assert_allclose(o, o_exp, rtol=0, atol=2e-3)
+        snap = snapshot(layer)
+        np.testing.assert_allclose(snap.scores[0], [float(Fraction(x)) for x in exp["scores"]],
+                                   rtol=1e-5, atol=1e-6)
+        np.testing.assert_array_equal(snap.pos[0], exp["kept_positions"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_full"])
+def test_tiny_workload(name):
+    """2 query heads / 1 KV head, d=64, T=16, 8 frames, B=32 (evictions) and
+    B=128 (no eviction: equals full causal attention)."""
+    spec = framegen.workload(name)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec)
+    _assert_reports(reports)
+    check_caches_bitwise(layer, ks, vs)
+    if name == "tiny_full":
+        # free-running GPU run == dense causal attention over the whole video
+        layer2 = _layer(spec)
+        for n in range(spec.n_frames):
+            o = layer2.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+            ref = full_causal_attention(qs[n], ks[: n + 1].reshape(-1, 1, 64),
+                                        vs[: n + 1].reshape(-1, 1, 64),
+                                        first_query=n * spec.frame_tokens)
+            maxabs, relrms = o_errors(o, ref)
+            assert maxabs <= O_MAXABS and relrms <= O_RELRMS, (n, maxabs, relrms)
+
+
+def test_1b_layer_free_running_and_teacher_forced():
+    """InternVL3-1B-like layer, 64 frames, B=1024, planted sinks."""
+    spec = framegen.workload("internvl3_1b_layer")
+    frames = framegen.stacked_frames(spec, workers=8)
+    qs, ks, vs = frames
+    layer, reports, _ = _run_teacher_forced(spec, frames=frames)
+    _assert_reports(reports, exact_select=False)
+    check_caches_bitwise(layer, ks, vs)
+    # free-running: GPU and oracle each follow their own trajectory
+    layer2 = _layer(spec)
+    orc = _oracle(spec)
+    _, sinks = framegen.sink_plan(spec)
+    match = total = 0
+    for n in range(spec.n_frames):
+        layer2.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+        ref = orc.step(qs[n], ks[n], vs[n])
+        snap = snapshot(layer2)
+        for h in range(spec.n_kv_heads):
+            kept = set(ref.kept_positions[h].tolist())
+            match += len(kept.intersection(snap.pos[h].tolist()))
+            total += len(kept)
+            seen = sinks[sinks < (n + 1) * spec.frame_tokens]
+            assert np.isin(seen, snap.pos[h]).all(), (n, h)
+    print(f"free-running selected-set agreement {match / total:.6f}")
+    assert match >= SELECT_AGREEMENT * total
+
+
+@pytest.mark.parametrize("shape", [
+    # (Hq, Hkv, d, T, B, frames): ragged T, B not a tile multiple, G=1, G=16, T=1
+    (6, 2, 128, 17, 50, 6),
+    (3, 3, 64, 100, 130, 4),
+    (16, 1, 64, 40, 64, 4),
+    (4, 2, 128, 1, 3, 7),
+    (12, 2, 128, 256, 2048, 12),
+    (8, 4, 64, 33, 1, 4),
+])
+def test_ragged_and_edge_shapes(shape):
+    Hq, Hkv, d, T, B, N = shape
+    spec = framegen.FrameSpec(Hq, Hkv, d, T, N, B, 1e4, 11, sinks=False)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec)
+    _assert_reports(reports, exact_select=False)
+    check_caches_bitwise(layer, ks, vs)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_explicit_split_counts(splits):
+    spec = framegen.workload("tiny").replace(n_q_heads=4, n_kv_heads=2, frame_tokens=48,
+                                             state_budget=100, n_frames=5)
+    layer = _layer(spec, num_splits=splits)
+    _, reports, _ = _run_teacher_forced(spec, layer=layer)
+    _assert_reports(reports, exact_select=False)
+
+
+def test_noncausal_frame_flag():
+    spec = framegen.workload("tiny").replace(n_frames=4)
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_NONCAUSAL_FRAME)
+    _, reports, _ = _run_teacher_forced(spec, layer=layer, orc_kw=dict(causal=False))
+    _assert_reports(reports, exact_select=False)
+
+
+def test_ring_detailed_cache_wraps():
+    spec = framegen.workload("tiny").replace(n_frames=5)
+    layer = skv.Layer(2, 1, 64, 16, 32, detailed_capacity=40, flags=skv.STATEKV_FLAG_D_RING)
+    qs, ks, vs = framegen.stacked_frames(spec)
+    for n in range(5):
+        layer.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+    torch.cuda.synchronize()
+    dc = layer.detailed_cache()
+    assert dc["length"] == 40 and dc["start"] == 80 - 40
+    from gpu_util import to_bits
+    dk = to_bits(dc["k"])[0]
+    allk = ks.reshape(-1, 1, 64)[:, 0]
+    for p in range(40, 80):
+        np.testing.assert_array_equal(dk[p % 40], allk[p])
+
+
+def test_capacity_error_leaves_layer_unchanged():
+    spec = framegen.workload("tiny").replace(n_frames=3)
+    layer = skv.Layer(2, 1, 64, 16, 32, detailed_capacity=32)
+    qs, ks, vs = framegen.stacked_frames(spec)
+    for n in range(2):
+        layer.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+    before = snapshot(layer)
+    with pytest.raises(skv.StateKVError) as e:
+        layer.prefill(to_dev(qs[2]), to_dev(ks[2]), to_dev(vs[2]))
+    assert e.value.status == -4
+    after = snapshot(layer)
+    assert layer.state()["frames_seen"] == 2
+    for h in range(1):
+        np.testing.assert_array_equal(before.pos[h], after.pos[h])
+
+
+def test_bitwise_determinism():
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=8)
+    qs, ks, vs = framegen.stacked_frames(spec, workers=8)
+    outs = []
+    for _ in range(2):
+        layer = _layer(spec)
+        os_ = [layer.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+               for n in range(spec.n_frames)]
+        snap = snapshot(layer)
+        outs.append((np.stack(os_), snap))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    for h in range(spec.n_kv_heads):
+        np.testing.assert_array_equal(outs[0][1].scores[h], outs[1][1].scores[h])
+        np.testing.assert_array_equal(outs[0][1].k[h], outs[1][1].k[h])
+        np.testing.assert_array_equal(outs[0][1].pos[h], outs[1][1].pos[h])

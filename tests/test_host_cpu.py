@@ -1,0 +1,113 @@
+"""Host logic and the C-ABI surface, on the CPU (no kernel is launched)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "statekv.h")
+CSRC = os.path.join(ROOT, "streaming_long_video_amd", "csrc")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(statekv_\w+)\(", text, re.M)))
+
+
+def test_plan_with_gxx_and_sanitizers(tmp_path):
+    exe = tmp_path / "plan_check"
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(ROOT, "tests", "cpp", "plan_check.cpp"), os.path.join(CSRC, "plan.cpp"),
+           "-o", str(exe)]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+skv = pytest.importorskip("streaming_long_video_amd")
+B = skv._binding
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    base = dict(n_q_heads=28, n_kv_heads=4, head_dim=128, frame_tokens=256, state_budget=4096,
+                detailed_capacity=131072)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def test_workspace_bytes_and_validation():
+    n = B.statekv_workspace_bytes(_cfg())
+    # two compressed states (K, V, positions), the detailed cache and scratch
+    assert n >= 2 * (2 * 4 * 4096 * 128 * 2 + 4 * 4096 * 8) + 2 * 4 * 131072 * 128 * 2
+    for bad, status in [(dict(head_dim=96), -2), (dict(n_kv_heads=5), -1),
+                        (dict(detailed_capacity=10), -1), (dict(state_budget=0), -1),
+                        (dict(flags=1), -2), (dict(flags=1 << 9), -1),
+                        (dict(state_budget=32600), -2), (dict(frame_tokens=5000), -2)]:
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_workspace_bytes(_cfg(**bad))
+        assert e.value.status == status, bad
+
+
+def test_init_views_and_argument_errors_are_host_side():
+    cfg = _cfg()
+    nbytes = B.statekv_workspace_bytes(cfg)
+    fake = 1 << 40  # never dereferenced: init and views are host only
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_init_layer(cfg, fake, nbytes - 1)
+    assert e.value.status == -3
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_init_layer(cfg, fake + 16, nbytes)
+    assert e.value.status == -3
+    h = B.statekv_init_layer(cfg, fake, nbytes)
+    st = B.statekv_state(h)
+    assert st.count == 0 and st.frames_seen == 0 and st.capacity == 4096 and st.last_pool == 0
+    assert fake <= st.k < fake + nbytes and fake <= st.pos < fake + nbytes
+    dc = B.statekv_detailed_cache(h)
+    assert dc.length == 0 and dc.capacity == 131072 and dc.start == 0
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_prefill_frame(h, 0, 0, 0, 0)
+    assert e.value.status == -1
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_prefill_frame(h, fake + 2, fake, fake, fake)
+    assert e.value.status == -1
+    B.statekv_reset_layer(h)
+    B.statekv_free_layer(h)
+
+
+def test_ring_layout_rejects_full_attention_before_any_launch():
+    cfg = _cfg(flags=B.STATEKV_FLAG_D_RING)
+    nbytes = B.statekv_workspace_bytes(cfg)
+    fake = 1 << 40
+    h = B.statekv_init_layer(cfg, fake, nbytes)
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_full_attention_frame(h, fake, fake, fake, fake)
+    assert e.value.status == -2
+    B.statekv_free_layer(h)
+
+
+def test_select_argument_errors():
+    with pytest.raises(B.StateKVError):
+        B.statekv_select_topb(0, 10, 5, 0)
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_select_topb(1 << 40, 40000, 5, 1 << 40)
+    assert e.value.status == -2
+    with pytest.raises(B.StateKVError):
+        B.statekv_select_topb(1 << 40, 0, 5, 1 << 40)
+
+
+def test_status_strings():
+    assert B.statekv_status_string(0) == "ok"
+    assert "capacity" in B.statekv_status_string(-4)
+    assert B.statekv_status_string(12345) == "unknown status"
