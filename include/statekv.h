@@ -135,7 +135,8 @@ int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace,
 /* The per-frame StateKV step (the four parts listed at the top) for the next
  * frame n = frames_seen: reads q/k/v, writes o, updates C and D, and advances
  * frames_seen.  Kernels: attention statistics pass, attention output + score
- * pass, split reduction, top-B select, gather + detailed-cache append. */
+ * pass, top-B select (with the split-O reduction in the same launch),
+ * gather + detailed-cache append. */
 int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
                           const void* v, float* o, void* stream);
 
@@ -164,8 +165,10 @@ const char* statekv_status_string(int status);
 enum {
   STATEKV_KERNEL_ATTN_STATS = 0, /* attention pass 1: row statistics           */
   STATEKV_KERNEL_ATTN_OUT = 1,   /* attention pass 2: O, importance partials   */
-  STATEKV_KERNEL_SPLIT_SUM = 2,  /* fixed-order sum of split O partials        */
-  STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select             */
+  STATEKV_KERNEL_SPLIT_SUM = 2,  /* full attention only: split combine (the
+                                    StateKV path sums its split O partials in
+                                    the SELECT launch)                          */
+  STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select + O split sum */
   STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append         */
   STATEKV_NUM_KERNELS = 5
 };

@@ -1,5 +1,5 @@
 // Fused GQA attention over the StateKV candidate pool [C_{n-1} ; frame n] for
-// gfx950, in two passes that share one tiling:
+// gfx950.  One kernel template, three passes sharing one tiling:
 //
 //   pass 1 (statistics): per query row, the max and the sum of exp of the
 //     logits over this workgroup's key split (online, per 32-key block);
@@ -7,28 +7,36 @@
 //     log-sum-exp, recomputes the logits, forms the normalised probabilities
 //     P, accumulates O = P V and the column sums of P (the candidates'
 //     importance, summed over the queries of every query head that shares the
-//     KV head).
+//     KV head);
+//   pass 3 (quadratic baseline): plain online-softmax attention of the frame
+//     over the whole detailed cache, no scores.
 //
-// The per-frame step these passes implement is the attention and importance
-// part of StateKV (paper.rainbus.top, method-steps section: softmax over the
+// What passes 1-2 implement is the attention and importance part of the
+// StateKV step (paper.rainbus.top, method-steps section: softmax over the
 // concatenated compressed memory and frame keys; a candidate's importance is
 // the sum over queries of its attention weight; paperlayer.ai App. A.3: cache
 // building needs the attention weights or sufficient statistics, which fused
 // attention kernels normally do not expose -- the row statistics of pass 1
 // are exactly those statistics).
 //
-// Layout of the work: the G query heads that share KV head h and the T frame
-// tokens form G*T query rows, cut into 32-token blocks of one head.  A
-// workgroup (4 waves) owns 8 such blocks (a row tile) and one contiguous split
-// of the pool's key tiles.  Logits are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16 (keys on M, queries on N): each lane then holds one
-// query and 16 keys, so the row statistics need no cross-lane work, the
-// probabilities feed the PV product O^T = V^T P^T
-// (v_mfma_f32_32x32x16_f16) straight from registers, and the column sums are
-// a short butterfly across the 32 lanes of each half-wave.  P enters PV as
-// fp16 scaled by 2^12 (11 significant bits, kept clear of fp16 subnormals);
-// V is converted bf16 -> fp16 (exact for |v| in [2^-17, 65504]) while it is
-// transposed into LDS.  Scores and O partials are written per split / row
+// Work layout: the G query heads that share KV head h and the T frame tokens
+// form G*T query rows, cut into 32-token blocks of one head.  A workgroup (8
+// waves, two per SIMD) owns 8 such blocks (a 256-row tile, one per wave) and
+// one contiguous split of the pool's 64-key tiles.  Key tiles are staged through
+// LDS double-buffered: the next tile's global loads are in flight in
+// registers while the current tile is computed, then written to the other
+// buffer (one barrier per tile).  Logits are computed transposed,
+// S^T = K Q^T, with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N): each
+// lane holds one query and 16 keys, so row statistics need no cross-lane
+// work, the probabilities feed O^T = V^T P^T (v_mfma_f32_32x32x16_f16)
+// straight from registers (A and B use the same permutation of the 16 key
+// slots), and the column sums are a reduce-scatter across the 32 lanes of each
+// half-wave (v_permlane16_swap, then bank-masked DPP).  P enters PV as fp16
+// scaled by 2^12 (11 significant bits, clear of fp16 subnormals); V is
+// converted bf16 -> fp16 (exact for |v| in [2^-17, 65504]) while it is
+// transposed into LDS.  Key blocks entirely inside the visible region take a
+// branch-free path; only blocks that reach the frame's causal triangle or the
+// pool's end are masked.  Scores and O partials are written per split / row
 // tile and reduced in a fixed order elsewhere: no atomics, bitwise
 // reproducible results.
 #include "../skv_internal.h"
@@ -37,16 +45,18 @@ namespace skv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kWaves = 8;        // two waves per SIMD
+constexpr int kQBlkPerWave = 1;  // 32-token query blocks per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kKPad = 8;  // bf16 padding per K row in LDS (conflict-free b128 reads)
 constexpr int kVPad = 4;  // fp16 padding per V^T row (conflict-free b64 reads)
-constexpr float kPUnscale = 1.f / 4096.f;
+constexpr float kPUnscale = 1.f / 4096.f;  // P is formed as 2^12 * P
 
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each
 // XCD gets a contiguous range of logical ids (consecutive ids share a KV head
@@ -56,51 +66,59 @@ __device__ inline int xcd_logical_id(int b, int n) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+__device__ inline float as_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ inline int as_i(float x) { return __builtin_bit_cast(int, x); }
+
+// DPP move of `src` into the lanes of `BANKS`; other lanes keep `old`.
+template <int CTRL, int BANKS>
+__device__ inline float dpp_into(float old, float src) {
+  return as_f(__builtin_amdgcn_update_dpp(as_i(old), as_i(src), CTRL, 0xF, BANKS, false));
+}
 template <int CTRL>
-__device__ inline float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+__device__ inline float dpp_all(float src) {
+  return as_f(__builtin_amdgcn_update_dpp(0, as_i(src), CTRL, 0xF, 0xF, true));
 }
 
-__device__ inline float swizzle_xor16(float x) {
-  // ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 (32-lane groups)
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
-}
-
-// Sum of v[r] over the 32 lanes of each half-wave, one key per lane pair.
-// Reduce-scatter butterfly: partners lane^16, lane^8 (row_ror:8), lane^7
-// (row_half_mirror), lane^2, lane^1 (quad_perm).  Lane l ends with the total
-// of register r = (l >> 1) & 15 (both lanes of a pair hold it).
-__device__ inline float colsum_reduce(float (&v)[16], int l32) {
-  const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+// Sum of v[r] over the 32 lanes of each half-wave (the 32 queries of a block),
+// reduce-scatter style.  Lane l ends with the total of register r = (l>>1)&15
+// (both lanes of a pair hold it).
+//   xor 16: v_permlane16_swap pairs (v[k], v[k+8]) across 16-lane rows;
+//   xor 8:  row_ror:8 into banks {0,1} / {2,3};
+//   xor 4:  row_shl:4 into banks {0,2}, row_shr:4 into banks {1,3};
+//   xor 2, xor 1: quad_perm.
+__device__ inline float colsum_reduce(const float (&v)[16], int l32) {
+  float w[8], x[4], y[2];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float send = b4 ? v[k] : v[k + 8];
-    const float keep = b4 ? v[k + 8] : v[k];
-    v[k] = keep + swizzle_xor16(send);
+    const auto s = __builtin_amdgcn_permlane16_swap(as_i(v[k]), as_i(v[k + 8]), false, false);
+    w[k] = as_f(s[0]) + as_f(s[1]);  // r = 8*b4 + k
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float send = b3 ? v[k] : v[k + 4];
-    const float keep = b3 ? v[k + 4] : v[k];
-    v[k] = keep + dpp<0x128>(send);
+    const float t = dpp_into<0x128, 0x3>(w[k + 4], w[k]);
+    const float u = dpp_into<0x128, 0xC>(w[k], w[k + 4]);
+    x[k] = t + u;  // r = 8*b4 + 4*b3 + k
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const float send = b2 ? v[k] : v[k + 2];
-    const float keep = b2 ? v[k + 2] : v[k];
-    v[k] = keep + dpp<0x141>(send);
+    const float t = dpp_into<0x104, 0x5>(x[k + 2], x[k]);
+    const float u = dpp_into<0x114, 0xA>(x[k], x[k + 2]);
+    y[k] = t + u;  // r = 8*b4 + 4*b3 + 2*b2 + k
   }
-  {
-    const float send = b1 ? v[0] : v[1];
-    const float keep = b1 ? v[1] : v[0];
-    v[0] = keep + dpp<0x4E>(send);
-  }
-  return v[0] + dpp<0xB1>(v[0]);
+  // cross-lane reads must run with every lane active: both before the select
+  const float p0 = dpp_all<0x4E>(y[0]);
+  const float p1 = dpp_all<0x4E>(y[1]);
+  const float z = (l32 & 2) ? y[1] + p1 : y[0] + p0;
+  return z + dpp_all<0xB1>(z);
 }
 
 __device__ inline float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ inline float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+__device__ inline uint32_t pack_f16(float a, float b) {
+  const f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // One 16-byte chunk (8 bf16) of pool row j, columns [col, col+8); zero past the pool.
 template <int D>
@@ -114,6 +132,63 @@ __device__ inline u32x4 pool_chunk(const uint16_t* state, const uint16_t* frame,
   return v;
 }
 
+// Registers staging one key tile between its global loads and its LDS stores.
+template <int D, bool WITH_V>
+struct TileStage {
+  static constexpr int KCH = kKeyTile * (D / 8) / kThreads;  // 16-B K chunks / thread
+  // (key pair, 8-column chunk) items of the V tile; at d = 64 there are fewer
+  // items than threads and the upper threads stage no V
+  static constexpr int VITEMS = (kKeyTile / 2) * (D / 8);
+  static constexpr int VIT = (VITEMS + kThreads - 1) / kThreads;  // items / thread
+  static constexpr bool VPART = VITEMS % kThreads != 0;
+  static_assert(KCH * kThreads == kKeyTile * (D / 8), "K tile must split evenly");
+  u32x4 k[KCH];
+  u32x4 v0[WITH_V ? VIT : 1], v1[WITH_V ? VIT : 1];
+
+  __device__ inline void load(const AttnArgs& a, int h, int pool, int key0, int tid) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      k[i] = pool_chunk<D>(a.kc, a.kf, a.ldc, a.Hkv, h, a.c, pool, key0 + ch / (D / 8),
+                           (ch % (D / 8)) * 8);
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + i * kThreads;
+        if (VPART && it >= VITEMS) continue;
+        const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
+        v0[i] = pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, a.c, pool, key0 + 2 * kp, dc);
+        v1[i] = pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, a.c, pool, key0 + 2 * kp + 1, dc);
+      }
+    }
+  }
+
+  // K rows as they are; V transposed to [d][key] and converted to fp16.
+  __device__ inline void store(uint16_t* Ks, _Float16* Vt, int tid) const {
+    constexpr int KLD = D + kKPad, VLD = kKeyTile + kVPad;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      *reinterpret_cast<u32x4*>(&Ks[(ch / (D / 8)) * KLD + (ch % (D / 8)) * 8]) = k[i];
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + i * kThreads;
+        if (VPART && it >= VITEMS) continue;
+        const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
+        uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[dc * VLD + 2 * kp]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          col[(2 * e) * (VLD / 2)] = pack_f16(bf16lo(v0[i][e]), bf16lo(v1[i][e]));
+          col[(2 * e + 1) * (VLD / 2)] = pack_f16(bf16hi(v0[i][e]), bf16hi(v1[i][e]));
+        }
+      }
+    }
+  }
+};
+
 template <int D, int PASS>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   constexpr int QB = kQBlkPerWave;
@@ -122,9 +197,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
   constexpr int KLD = D + kKPad;
   constexpr int VLD = KT + kVPad;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KLD];
-  __shared__ __attribute__((aligned(16))) _Float16 Vt[PASS >= 2 ? D * VLD : 8];
-  __shared__ float sigw[PASS == 2 ? kWaves * KT : 1];
+  constexpr bool WITH_V = PASS >= 2;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[WITH_V ? 2 : 1][WITH_V ? D * VLD : 8];
+  __shared__ float sigw[PASS == 2 ? 2 : 1][PASS == 2 ? kWaves * KT : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -144,8 +220,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // This wave's query blocks: block b = tb*G + gl holds tokens [32tb, 32tb+32)
   // of query head h*G + gl.  Lane l32 owns token 32tb + l32 of each block.
   const int b0 = rtile * kRowBlk;
-  int qtok[QB], qhead[QB];
-  int wave_tmax = -1;
+  int qtok[QB], qhead[QB], qlim[QB];
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
     const int b = b0 + w * QB + i;
@@ -156,13 +231,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const int t = tb * kTokBlk + l32;
       qtok[i] = t < a.T ? t : -1;
       qhead[i] = h * a.G + b % a.G;
-      wave_tmax = max(wave_tmax, min(a.T - 1, tb * kTokBlk + kTokBlk - 1));
     }
+    // frame key t' is visible to this lane's query iff t' <= qlim
+    qlim[i] = qtok[i] < 0 ? -1 : (a.causal ? qtok[i] : a.T - 1);
   }
   const int blast = min(b0 + kRowBlk, a.nqblk) - 1;
   const int wg_tmax = min(a.T - 1, (blast / a.G) * kTokBlk + kTokBlk - 1);
   const int wg_klim = a.causal ? c + wg_tmax + 1 : pool;
-  const int wave_klim = wave_tmax < 0 ? 0 : (a.causal ? c + wave_tmax + 1 : pool);
   const int tile_end = max(tile_lo, min(tile_hi, (wg_klim + KT - 1) / KT));
 
   bf16x8 qreg[QB][NKK];
@@ -179,14 +254,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 
   float mrun[QB], lrun[QB], lse2[QB];
-  f32x16 oacc[QB][NMB];
+  f32x16 oacc[WITH_V ? QB : 1][WITH_V ? NMB : 1];
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
     mrun[i] = -INFINITY;
     lrun[i] = 0.f;
     lse2[i] = INFINITY;
+  }
+  if constexpr (WITH_V) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] = f32x16{};
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] = f32x16{};
   }
   if constexpr (PASS == 2) {
     // Row log-sum-exp (base 2, scaled logits) from the split statistics,
@@ -197,9 +276,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const int64_t row = (int64_t)qhead[i] * a.tpad + qtok[i];
       const int64_t stride = (int64_t)a.Hq * a.tpad;
       float M = -INFINITY;
-      for (int sp = 0; sp < a.S; ++sp) M = fmaxf(M, a.m_part[sp * stride + row]);
+      for (int sp = 0; sp < a.Sst; ++sp) M = fmaxf(M, a.m_part[sp * stride + row]);
       float L = 0.f;
-      for (int sp = 0; sp < a.S; ++sp) {
+      for (int sp = 0; sp < a.Sst; ++sp) {
         const float ms = a.m_part[sp * stride + row];
         if (ms > -INFINITY) L += a.l_part[sp * stride + row] * exp2f((ms - M) * sl2);
       }
@@ -207,167 +286,199 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
   }
 
-  auto emit_scores = [&](int tile) {
+  // -- per-32-key-block work -----------------------------------------------
+  // register r of query block i holds frame offset kbase - c + 8(r/4) + 4 half
+  // + r%4 of its key, visible iff that offset does not exceed qlim[i]
+  auto visible = [&](int kbase, int i, int r) {
+    return 8 * (r >> 2) + (r & 3) <= qlim[i] - (kbase - c + 4 * half);
+  };
+
+  auto qk_block = [&](const uint16_t* K, int kb, f32x16 (&sacc)[QB]) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) sacc[i] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 ak =
+          *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + l32) * KLD + kk * 16 + half * 8]);
+#pragma unroll
+      for (int i = 0; i < QB; ++i)
+        sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[i][kk], sacc[i], 0, 0, 0);
+    }
+  };
+
+  auto pv_block = [&](const _Float16* V, int kb, const u32x4 (&ph)[QB][2]) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab) {
+        const _Float16* vrow = &V[(mb * 32 + l32) * VLD + kb * 32 + slab * 16 + 4 * half];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int i = 0; i < QB; ++i)
+          oacc[i][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, ph[i][slab]),
+              oacc[i][mb], 0, 0, 0);
+      }
+    }
+  };
+
+  // pass 1: online row max / sum of exp over this block
+  auto stats_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      float z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        z[r] = (!masked || visible(kbase, i, r)) ? sacc[i][r] : -INFINITY;
+      float m8[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m8[r] = fmaxf(z[2 * r], z[2 * r + 1]);
+      const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                             fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+      const float mnew = fmaxf(mrun[i], mx);
+      // nothing visible yet for this lane: every exp below is exp2(-inf) = 0
+      const float ms = (mnew == -INFINITY ? 0.f : mnew) * sl2;
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
+#pragma unroll
+      for (int st = 8; st >= 1; st >>= 1)
+#pragma unroll
+        for (int r = 0; r < st; ++r) e[r] += e[r + st];
+      lrun[i] = lrun[i] * __builtin_amdgcn_exp2f(fmaf(mrun[i], sl2, -ms)) + e[0];
+      mrun[i] = mnew;
+    }
+  };
+
+  // pass 2: normalised P (x 2^12) -> fp16 pairs, column sums -> LDS
+  auto scores_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked, int kb,
+                          float* sw, u32x4 (&ph)[QB][2]) {
+    float p[QB][16];
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(sacc[i][r], sl2, -lse2[i]));
+        p[i][r] = (!masked || visible(kbase, i, r)) ? e : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < QB; ++i)
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          ph[i][slab][m] = pack_f16(p[i][slab * 8 + 2 * m], p[i][slab * 8 + 2 * m + 1]);
+    float cs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      cs[r] = p[0][r];
+#pragma unroll
+      for (int i = 1; i < QB; ++i) cs[r] += p[i][r];
+    }
+    const float tot = colsum_reduce(cs, l32);
+    if (!(l32 & 1)) {
+      const int r = l32 >> 1;
+      sw[w * KT + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = tot * kPUnscale;
+    }
+  };
+
+  // pass 3: online softmax with rescaled O (quadratic baseline)
+  auto online_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked,
+                          u32x4 (&ph)[QB][2]) {
+#pragma unroll
+    for (int i = 0; i < QB; ++i) {
+      float z[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = (!masked || visible(kbase, i, r)) ? sacc[i][r] : -INFINITY;
+        mx = fmaxf(mx, z[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));  // both half-waves hold the same query
+      const float mnew = fmaxf(mrun[i], mx);
+      // nothing visible yet for this query: every exp below is exp2(-inf) = 0
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f((mrun[i] - msafe) * sl2);
+      const float ms = fmaf(msafe, sl2, -12.f);
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          ph[i][slab][m] = pack_f16(e[slab * 8 + 2 * m], e[slab * 8 + 2 * m + 1]);
+#pragma unroll
+      for (int st = 8; st >= 1; st >>= 1)
+#pragma unroll
+        for (int r = 0; r < st; ++r) e[r] += e[r + st];
+      lrun[i] = lrun[i] * alpha + e[0];
+      mrun[i] = mnew;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= alpha;
+    }
+  };
+
+  auto emit_scores = [&](int tile, const float* sw) {
     if constexpr (PASS == 2) {
       if (tid < KT) {
         const int j = tile * KT + tid;
         if (j < pool) {
           float acc = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) acc += sigw[ww * KT + tid];
+          for (int ww = 0; ww < kWaves; ++ww) acc += sw[ww * KT + tid];
           a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = acc;
         }
       }
     }
   };
 
-  for (int tile = tile_lo; tile < tile_end; ++tile) {
-    const int key0 = tile * KT;
-    __syncthreads();  // LDS tiles free; previous tile's sigw complete
-    if (tile > tile_lo) emit_scores(tile - 1);
-    for (int ch = tid; ch < KT * (D / 8); ch += kThreads) {
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&Ks[row * KLD + col]) =
-          pool_chunk<D>(a.kc, a.kf, a.ldc, a.Hkv, h, c, pool, key0 + row, col);
-    }
-    if constexpr (PASS >= 2) {
-      for (int it = tid; it < (KT / 2) * (D / 8); it += kThreads) {
-        const int kp = it % (KT / 2), dc = (it / (KT / 2)) * 8;
-        const u32x4 v0 = pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, c, pool, key0 + 2 * kp, dc);
-        const u32x4 v1 =
-            pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, c, pool, key0 + 2 * kp + 1, dc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          f16x2 lo = {(_Float16)bf16lo(v0[e]), (_Float16)bf16lo(v1[e])};
-          f16x2 hi = {(_Float16)bf16hi(v0[e]), (_Float16)bf16hi(v1[e])};
-          *reinterpret_cast<f16x2*>(&Vt[(dc + 2 * e) * VLD + 2 * kp]) = lo;
-          *reinterpret_cast<f16x2*>(&Vt[(dc + 2 * e + 1) * VLD + 2 * kp]) = hi;
-        }
-      }
-    }
+  // -- the tile loop (double-buffered LDS, one barrier per tile) -------------
+  TileStage<D, WITH_V> stage;
+  if (tile_end > tile_lo) {
+    stage.load(a, h, pool, tile_lo * KT, tid);
+    stage.store(Ks[0], Vt[0], tid);
     __syncthreads();
-
+  }
+  for (int tile = tile_lo; tile < tile_end; ++tile) {
+    const int cur = (tile - tile_lo) & 1;
+    const int key0 = tile * KT;
+    const bool more = tile + 1 < tile_end;
+    if (more) stage.load(a, h, pool, key0 + KT, tid);
+    if constexpr (PASS == 2) {
+      if (tile > tile_lo) emit_scores(tile - 1, sigw[cur ^ 1]);
+    }
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
       const int kbase = key0 + kb * 32;
-      float cs[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cs[r] = 0.f;
-      if (kbase < wave_klim) {
-        f32x16 sacc[QB];
-#pragma unroll
-        for (int i = 0; i < QB; ++i) sacc[i] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 ak =
-              *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * KLD + kk * 16 + half * 8]);
-#pragma unroll
-          for (int i = 0; i < QB; ++i)
-            sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[i][kk], sacc[i], 0, 0, 0);
-        }
-        // lane holds S^T[key = kbase + 8(r/4) + 4 half + r%4][query qtok]
-        if constexpr (PASS == 1) {
-#pragma unroll
-          for (int i = 0; i < QB; ++i) {
-            float z[16];
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = kbase + 8 * (r >> 2) + 4 * half + (r & 3);
-              const bool vis = j < pool && (j < c || !a.causal || j - c <= qtok[i]);
-              z[r] = vis ? sacc[i][r] : -INFINITY;
-              mx = fmaxf(mx, z[r]);
-            }
-            if (mx > -INFINITY) {
-              const float mnew = fmaxf(mrun[i], mx);
-              const float ms = mnew * sl2;
-              float sum = 0.f;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
-              lrun[i] = lrun[i] * __builtin_amdgcn_exp2f(fmaf(mrun[i], sl2, -ms)) + sum;
-              mrun[i] = mnew;
-            }
-          }
-        } else {
-          f16x8 ph[QB][2];
-          if constexpr (PASS == 2) {
-#pragma unroll
-            for (int i = 0; i < QB; ++i) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int j = kbase + 8 * (r >> 2) + 4 * half + (r & 3);
-                const bool vis = j < pool && (j < c || !a.causal || j - c <= qtok[i]);
-                const float p =
-                    vis ? __builtin_amdgcn_exp2f(fmaf(sacc[i][r], sl2, -lse2[i])) : 0.f;
-                cs[r] += p;
-                ph[i][r >> 3][r & 7] = (_Float16)p;
-              }
-            }
-          } else {
-            // online softmax: running max shared by the two half-waves that
-            // hold the same query; O^T and l rescaled when the max grows
-#pragma unroll
-            for (int i = 0; i < QB; ++i) {
-              float z[16];
-              float mx = -INFINITY;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int j = kbase + 8 * (r >> 2) + 4 * half + (r & 3);
-                const bool vis = j < pool && (j < c || !a.causal || j - c <= qtok[i]);
-                z[r] = vis ? sacc[i][r] : -INFINITY;
-                mx = fmaxf(mx, z[r]);
-              }
-              mx = fmaxf(mx, __shfl_xor(mx, 32));
-              const float mnew = fmaxf(mrun[i], mx);
-              if (mnew == -INFINITY) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) ph[i][r >> 3][r & 7] = (_Float16)0.f;
-                continue;
-              }
-              const float alpha = __builtin_amdgcn_exp2f((mrun[i] - mnew) * sl2);
-              const float ms = fmaf(mnew, sl2, -12.f);
-              float sum = 0.f;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
-                sum += p;
-                ph[i][r >> 3][r & 7] = (_Float16)p;
-              }
-              lrun[i] = lrun[i] * alpha + sum;
-              mrun[i] = mnew;
-#pragma unroll
-              for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= alpha;
-            }
-          }
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-            for (int slab = 0; slab < 2; ++slab) {
-              const _Float16* vrow = &Vt[(mb * 32 + l32) * VLD + kb * 32 + slab * 16 + 4 * half];
-              const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow);
-              const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + 8);
-              const f16x8 av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-              for (int i = 0; i < QB; ++i)
-                oacc[i][mb] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_f16(av, ph[i][slab], oacc[i][mb], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if constexpr (PASS == 2) {
-        const float tot = colsum_reduce(cs, l32);
-        if (!(l32 & 1)) {
-          const int r = l32 >> 1;
-          sigw[w * KT + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3)] = tot * kPUnscale;
-        }
+      // blocks inside the state (or, without the causal mask, inside the
+      // pool) are fully visible to every query
+      const bool masked = a.causal ? (kbase + 32 > c) : (kbase + 32 > pool);
+      f32x16 sacc[QB];
+      qk_block(Ks[cur], kb, sacc);
+      if constexpr (PASS == 1) {
+        if (masked) stats_block(sacc, kbase, true);
+        else stats_block(sacc, kbase, false);
+      } else if constexpr (PASS == 2) {
+        u32x4 ph[QB][2];
+        if (masked) scores_block(sacc, kbase, true, kb, sigw[cur], ph);
+        else scores_block(sacc, kbase, false, kb, sigw[cur], ph);
+        pv_block(Vt[cur], kb, ph);
+      } else {
+        u32x4 ph[QB][2];
+        if (masked) online_block(sacc, kbase, true, ph);
+        else online_block(sacc, kbase, false, ph);
+        pv_block(Vt[cur], kb, ph);
       }
     }
+    if (more) stage.store(Ks[cur ^ 1], Vt[WITH_V ? cur ^ 1 : 0], tid);
+    __syncthreads();
   }
 
   if constexpr (PASS == 2) {
-    __syncthreads();
-    if (tile_end > tile_lo) emit_scores(tile_end - 1);
+    if (tile_end > tile_lo) emit_scores(tile_end - 1, sigw[(tile_end - 1 - tile_lo) & 1]);
     // key tiles of this split that no query of the row tile can see
     for (int j = tile_end * KT + tid; j < min(tile_hi * KT, pool); j += kThreads)
       a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = 0.f;
@@ -392,32 +503,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const float lt = lrun[i] + __shfl_xor(lrun[i], 32);  // both halves: same running max
       if (qtok[i] < 0) continue;
       const int64_t row = (int64_t)qtok[i] * a.Hq + qhead[i];
-      if (a.S == 1) {
-        const float inv = 1.f / lt;
-        float* dst = a.o_out + row * D;
+      const bool direct = a.S == 1;
+      const float scale = direct ? 1.f / lt : kPUnscale;
+      float* dst = a.o_out + ((direct ? 0 : (int64_t)s * a.T * a.Hq) + row) * D;
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+      for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
-                       oacc[i][mb][4 * q4 + 3]};
-            *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * q4 + 4 * half) = v * inv;
-          }
-      } else {
-        float* dst = a.o_out + ((int64_t)s * a.T * a.Hq + row) * D;
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
-                       oacc[i][mb][4 * q4 + 3]};
-            *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * q4 + 4 * half) = v * kPUnscale;
-          }
-        if (half == 0) {
-          const int64_t idx = ((int64_t)s * a.Hq + qhead[i]) * a.tpad + qtok[i];
-          a.m_part[idx] = mrun[i];
-          a.l_part[idx] = lt * kPUnscale;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
+                     oacc[i][mb][4 * q4 + 3]};
+          *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * q4 + 4 * half) = v * scale;
         }
+      if (!direct && half == 0) {
+        const int64_t idx = ((int64_t)s * a.Hq + qhead[i]) * a.tpad + qtok[i];
+        a.m_part[idx] = mrun[i];
+        a.l_part[idx] = lt * kPUnscale;
       }
     }
   } else {
@@ -435,16 +535,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         a.l_part[idx] = L;
       }
     }
-  }
-}
-
-__global__ __launch_bounds__(256) void split_sum_kernel(const f32x4* part, int S, int64_t n4,
-                                                        f32x4* o) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    f32x4 acc = part[i];
-    for (int sp = 1; sp < S; ++sp) acc += part[sp * n4 + i];
-    o[i] = acc;
   }
 }
 
@@ -479,14 +569,27 @@ __global__ __launch_bounds__(256) void full_combine_kernel(AttnArgs a, float* o)
 
 namespace {
 int attn_grid(const AttnArgs& a) { return a.Hkv * a.S * a.rt; }
+
+template <int PASS>
+hipError_t launch_pass(const AttnArgs& a, int D, hipStream_t st) {
+  if (D == 128)
+    hipLaunchKernelGGL((attn_kernel<128, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<64, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
 }  // namespace
 
+hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st) {
+  return launch_pass<1>(a, D, st);
+}
+
+hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st) {
+  return launch_pass<2>(a, D, st);
+}
+
 hipError_t launch_full_attn(const AttnArgs& a, int D, hipStream_t st) {
-  if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, 3>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, 3>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_pass<3>(a, D, st);
 }
 
 hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, hipStream_t st) {
@@ -497,32 +600,6 @@ hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, hipStream_t s
     hipLaunchKernelGGL((full_combine_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, a, o);
   else
     hipLaunchKernelGGL((full_combine_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, a, o);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st) {
-  if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, 1>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, 1>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st) {
-  if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, 2>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_kernel<64, 2>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_split_sum(const float* part, int S, int64_t n, float* o, hipStream_t st) {
-  const int64_t n4 = n / 4;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     reinterpret_cast<const f32x4*>(part), S, n4, reinterpret_cast<f32x4*>(o));
   return hipGetLastError();
 }
 

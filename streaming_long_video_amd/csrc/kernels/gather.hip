@@ -10,8 +10,10 @@
 //     (rainbus method steps: after frame n the frame's keys/values join the
 //     detailed state, which keeps every video token for decoding).
 //
-// Both are row copies of d bf16 (128 or 256 bytes): 16-byte vector loads and
-// stores, consecutive threads on consecutive 16-byte chunks of a row.
+// Both are copies of d-element bf16 rows.  A workgroup moves 32 rows (K and
+// V); every thread issues all of its 16-byte loads before its stores (4 in
+// flight per thread at d = 128), consecutive threads on consecutive 16-byte
+// chunks of a row.
 #include "../skv_internal.h"
 
 namespace skv {
@@ -24,32 +26,43 @@ constexpr int kRowsPerBlock = 32;
 template <int D>
 __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs g,
                                                                      int gather_blocks) {
-  constexpr int CH = D / 8;  // 16-byte chunks per row
+  constexpr int CH = D / 8;                                    // 16-byte chunks per row
+  constexpr int PER = 2 * kRowsPerBlock * CH / kCopyThreads;  // chunks per thread (K and V)
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  u32x4 buf[PER];
   if (b < gather_blocks) {
     const int per_h = (g.newc + kRowsPerBlock - 1) / kRowsPerBlock;
     const int h = b / per_h;
     const int s0 = (b % per_h) * kRowsPerBlock;
     const int rows = min(kRowsPerBlock, g.newc - s0);
-    for (int it = tid; it < 2 * rows * CH; it += kCopyThreads) {
-      const int which = it / (rows * CH);  // 0: keys, 1: values
-      const int rem = it % (rows * CH);
-      const int s = s0 + rem / CH, col = (rem % CH) * 8;
-      const int j = g.keep_all ? s : g.sel[(int64_t)h * g.B + s];
-      const uint16_t* src;
-      if (j < g.c)
-        src = (which ? g.vc_prev : g.kc_prev) + ((int64_t)h * g.B + j) * D + col;
-      else
-        src = (which ? g.vf : g.kf) + ((int64_t)(j - g.c) * g.Hkv + h) * D + col;
-      uint16_t* dst = (which ? g.vc_next : g.kc_next) + ((int64_t)h * g.B + s) * D + col;
-      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-    }
+    const int32_t* sel = g.sel + (int64_t)h * g.B + s0;
     if (tid < rows) {
-      const int s = s0 + tid;
-      const int j = g.keep_all ? s : g.sel[(int64_t)h * g.B + s];
-      g.pos_next[(int64_t)h * g.B + s] =
+      const int j = g.keep_all ? s0 + tid : sel[tid];
+      g.pos_next[(int64_t)h * g.B + s0 + tid] =
           j < g.c ? g.pos_prev[(int64_t)h * g.B + j] : g.pos_offset + g.frame_base + (j - g.c);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = tid + i * kCopyThreads;
+      const int which = it / (kRowsPerBlock * CH);  // 0: keys, 1: values
+      const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
+      if (r < rows) {
+        const int j = g.keep_all ? s0 + r : sel[r];
+        const uint16_t* p =
+            j < g.c ? (which ? g.vc_prev : g.kc_prev) + ((int64_t)h * g.B + j) * D + col
+                    : (which ? g.vf : g.kf) + ((int64_t)(j - g.c) * g.Hkv + h) * D + col;
+        buf[i] = *reinterpret_cast<const u32x4*>(p);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int it = tid + i * kCopyThreads;
+      const int which = it / (kRowsPerBlock * CH);
+      const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
+      if (r < rows)
+        *reinterpret_cast<u32x4*>((which ? g.vc_next : g.kc_next) +
+                                  ((int64_t)h * g.B + s0 + r) * D + col) = buf[i];
     }
     return;
   }
@@ -59,15 +72,26 @@ __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs 
   const int h = ab / per_h;
   const int t0 = (ab % per_h) * kRowsPerBlock;
   const int rows = min(kRowsPerBlock, g.T - t0);
-  for (int it = tid; it < 2 * rows * CH; it += kCopyThreads) {
-    const int which = it / (rows * CH);
-    const int rem = it % (rows * CH);
-    const int t = t0 + rem / CH, col = (rem % CH) * 8;
-    int64_t slot = g.frame_base + t;
-    if (g.ring) slot %= g.cap;
-    const uint16_t* src = (which ? g.vf : g.kf) + ((int64_t)t * g.Hkv + h) * D + col;
-    uint16_t* dst = (which ? g.vd : g.kd) + ((int64_t)h * g.cap + slot) * D + col;
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int it = tid + i * kCopyThreads;
+    const int which = it / (kRowsPerBlock * CH);
+    const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
+    if (r < rows)
+      buf[i] = *reinterpret_cast<const u32x4*>((which ? g.vf : g.kf) +
+                                               ((int64_t)(t0 + r) * g.Hkv + h) * D + col);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int it = tid + i * kCopyThreads;
+    const int which = it / (kRowsPerBlock * CH);
+    const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
+    if (r < rows) {
+      int64_t slot = g.frame_base + t0 + r;
+      if (g.ring) slot %= g.cap;
+      *reinterpret_cast<u32x4*>((which ? g.vd : g.kd) + ((int64_t)h * g.cap + slot) * D + col) =
+          buf[i];
+    }
   }
 }
 

@@ -1,4 +1,5 @@
-// Top-B selection over the candidate pool, one workgroup per KV head.
+// Top-B selection over the candidate pool, one workgroup per KV head, in the
+// same launch as the fixed-order sum of the attention's split O partials.
 //
 // StateKV refreshes the compressed state by keeping the B candidates of the
 // pool (previous state plus the frame's tokens) with the largest importance
@@ -7,12 +8,15 @@
 // ascending position, that is the lower pool index.
 //
 // Scores are non-negative fp32, so their bit patterns order like the values
-// (NaN and negative patterns are mapped to 0).  The threshold tau = the B-th
-// largest key is found by an MSB-first radix select (four 8-bit digits, LDS
-// histograms, a descending exclusive scan per digit).  The kept set is every
-// key > tau plus the first k keys == tau in pool order, compacted with one
-// block-wide scan so the output lists pool indices in ascending order.  Only
-// integer operations decide the result, so it is exact and deterministic.
+// (NaN and negative patterns are mapped to 0).  The threshold is found by an
+// MSB-first radix select over the bits below the highest bit in which the
+// pool's keys differ (so the first 8-bit digit already spreads the keys over
+// the histogram), with one histogram per wave to keep LDS atomics on distinct
+// addresses.  After each digit, if every key of the boundary bin is needed the
+// search stops early.  The kept set is every key above the boundary plus the
+// first k keys of the boundary bin in pool order, compacted with one
+// workgroup scan so the output lists pool indices in ascending order.  Only
+// integer operations decide the result: exact and deterministic.
 #include "../skv_internal.h"
 
 namespace skv {
@@ -20,13 +24,15 @@ namespace skv {
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline uint32_t score_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return u > 0x7F800000u ? 0u : u;  // NaN, -0 and negatives rank lowest
 }
 
-// Exclusive prefix sum over the workgroup (all threads must call it).
-__device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh) {
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   uint32_t v = x;
 #pragma unroll
@@ -36,83 +42,162 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh) {
   }
   if (lane == 63) sh[w] = v;
   __syncthreads();
-  if (w == 0) {
-    uint32_t t = lane < kSelWaves ? sh[lane] : 0u;
+  uint32_t base = 0, tot = 0;
 #pragma unroll
-    for (int o = 1; o < kSelWaves; o <<= 1) {
-      const uint32_t y = __shfl_up(t, o);
-      if (lane >= o) t += y;
-    }
-    if (lane < kSelWaves) sh[lane] = t;
+  for (int i = 0; i < kSelWaves; ++i) {
+    const uint32_t s = sh[i];
+    if (i < w) base += s;
+    tot += s;
   }
   __syncthreads();
-  const uint32_t base = w ? sh[w - 1] : 0u;
-  __syncthreads();
+  if (total) *total = tot;
   return base + v - x;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* sig_part, int rt,
-                                                             int ldsig, int pool, int budget,
-                                                             float* scores, int ldscores,
-                                                             int32_t* sel, int ldsel) {
-  extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan_sh[kSelWaves];
-  __shared__ uint32_t found_digit, found_excl;
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const float* sp = sig_part + (int64_t)h * rt * ldsig;
-  int32_t* out = sel + (int64_t)h * ldsel;
+__device__ inline uint32_t block_min_max(uint32_t mn, uint32_t mx, uint32_t* sh, uint32_t* out_max) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh[w] = mn;
+    sh[kSelWaves + w] = mx;
+  }
+  __syncthreads();
+  uint32_t a = sh[0], b = sh[kSelWaves];
+#pragma unroll
+  for (int i = 1; i < kSelWaves; ++i) {
+    a = min(a, sh[i]);
+    b = max(b, sh[kSelWaves + i]);
+  }
+  __syncthreads();
+  *out_max = b;
+  return a;
+}
 
-  // importance = sum of the row tiles' partial column sums, in tile order
-  for (int j = tid; j < pool; j += kSelThreads) {
-    float acc = sp[j];
-    for (int r = 1; r < rt; ++r) acc += sp[(int64_t)r * ldsig + j];
-    if (scores) scores[(int64_t)h * ldscores + j] = acc;
-    keys[j] = score_key(acc);
+struct SelectJob {
+  const float* sig_part;  // [Hkv][rt][ldsig] partial scores (rt = 1: plain scores)
+  int rt, ldsig, pool, budget;
+  float* scores;          // [Hkv][ldscores] summed scores (may be null)
+  int ldscores;
+  int32_t* sel;           // [Hkv][ldsel] kept pool indices, ascending
+  int ldsel;
+};
+
+struct SumJob {
+  const f32x4* part;      // [S][n4]
+  f32x4* out;             // [n4]
+  int64_t n4;
+  int S;
+};
+
+__device__ void select_one_head(const SelectJob& J, int h) {
+  extern __shared__ uint32_t keys[];
+  __shared__ uint32_t whist[kSelWaves][256];
+  __shared__ uint32_t red[2 * kSelWaves];
+  __shared__ uint32_t found[3];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int pool = J.pool, budget = J.budget;
+  const float* sp = J.sig_part + (int64_t)h * J.rt * J.ldsig;
+  int32_t* out = J.sel + (int64_t)h * J.ldsel;
+
+  // importance = sum of the row tiles' partial column sums, in tile order;
+  // kLoad candidates per thread per round, all their partials loaded first
+  constexpr int kLoad = 4;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int j0 = 0; j0 < pool; j0 += kLoad * kSelThreads) {
+    float acc[kLoad];
+#pragma unroll
+    for (int q = 0; q < kLoad; ++q) {
+      const int j = min(j0 + tid + q * kSelThreads, pool - 1);
+      acc[q] = sp[j];
+    }
+    for (int r = 1; r < J.rt; ++r) {
+      float part[kLoad];
+#pragma unroll
+      for (int q = 0; q < kLoad; ++q) {
+        const int j = min(j0 + tid + q * kSelThreads, pool - 1);
+        part[q] = sp[(int64_t)r * J.ldsig + j];
+      }
+#pragma unroll
+      for (int q = 0; q < kLoad; ++q) acc[q] += part[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kLoad; ++q) {
+      const int j = j0 + tid + q * kSelThreads;
+      if (j < pool) {
+        if (J.scores) J.scores[(int64_t)h * J.ldscores + j] = acc[q];
+        const uint32_t u = score_key(acc[q]);
+        keys[j] = u;
+        mn = min(mn, u);
+        mx = max(mx, u);
+      }
+    }
   }
   if (pool <= budget) {
     for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
     return;
   }
-  __syncthreads();
+  uint32_t kmax;
+  const uint32_t kmin = block_min_max(mn, mx, red, &kmax);  // also orders keys[] writes
 
-  uint32_t prefix = 0u, pmask = 0u;
+  // radix select below the common prefix of all keys
+  uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
   uint32_t k = (uint32_t)budget;  // rank (from the top) still to place
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0u;
+  int hb = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
+  if (hb >= 0) {
+    pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    prefix = kmin & pmask;
+  }
+  while (hb >= 0) {
+    const int shift = hb >= 7 ? hb - 7 : 0;
+    const uint32_t dmask = (2u << (hb - shift)) - 1u;  // digit bits [shift, hb]
+    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&whist[0][0])[i] = 0u;
     __syncthreads();
     for (int j = tid; j < pool; j += kSelThreads) {
       const uint32_t u = keys[j];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+      if ((u & pmask) == prefix) atomicAdd(&whist[w][(u >> shift) & dmask], 1u);
     }
     __syncthreads();
-    const uint32_t cnt = tid < 256 ? hist[255 - tid] : 0u;  // descending digits
-    const uint32_t excl = block_exclusive_scan(cnt, scan_sh);
-    if (tid < 256 && excl < k && k <= excl + cnt) {
-      found_digit = 255u - tid;
-      found_excl = excl;
+    const uint32_t d = 255u - (uint32_t)tid;  // descending digits (tid < 256)
+    uint32_t cnt = 0;
+    if (tid < 256 && d <= dmask) {
+#pragma unroll
+      for (int i = 0; i < kSelWaves; ++i) cnt += whist[i][d];
+    }
+    const uint32_t excl = block_exclusive_scan(cnt, red, nullptr);
+    if (tid < 256 && cnt && excl < k && k <= excl + cnt) {
+      found[0] = d;
+      found[1] = excl;
+      found[2] = cnt;
     }
     __syncthreads();
-    prefix |= found_digit << shift;
-    pmask |= 0xFFu << shift;
-    k -= found_excl;
+    prefix |= found[0] << shift;
+    pmask |= dmask << shift;
+    k -= found[1];
+    const uint32_t bin = found[2];
     __syncthreads();
+    if (bin == k) break;  // the whole boundary bin is kept: no tie to break
+    hb = shift - 1;
   }
-  // keep keys > tau, and the first k keys == tau in pool order
+
+  // keep (u & pmask) > prefix, and the first k keys with (u & pmask) == prefix
   const int per = (pool + kSelThreads - 1) / kSelThreads;
   const int j0 = min(pool, tid * per), j1 = min(pool, j0 + per);
   uint32_t ngt = 0u, neq = 0u;
   for (int j = j0; j < j1; ++j) {
-    const uint32_t u = keys[j];
+    const uint32_t u = keys[j] & pmask;
     ngt += u > prefix;
     neq += u == prefix;
   }
-  const uint32_t packed = block_exclusive_scan(ngt | (neq << 16), scan_sh);
+  const uint32_t packed = block_exclusive_scan(ngt | (neq << 16), red, nullptr);
   const uint32_t gt_before = packed & 0xFFFFu, eq_before = packed >> 16;
   uint32_t slot = gt_before + min(eq_before, k);
   uint32_t eqr = eq_before;
   for (int j = j0; j < j1; ++j) {
-    const uint32_t u = keys[j];
+    const uint32_t u = keys[j] & pmask;
     if (u > prefix) {
       out[slot++] = j;
     } else if (u == prefix) {
@@ -122,21 +207,54 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* sig_pa
   }
 }
 
-hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
-                         int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
-                         hipStream_t st) {
+// Blocks [0, n_select) select one KV head each; the remaining blocks sum the
+// split O partials (grid-stride over their share).
+__global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, int n_select,
+                                                                 SumJob Sj) {
+  if ((int)blockIdx.x < n_select) {
+    select_one_head(J, blockIdx.x);
+    return;
+  }
+  const int64_t nb = gridDim.x - n_select;
+  for (int64_t i = (int64_t)(blockIdx.x - n_select) * kSelThreads + threadIdx.x; i < Sj.n4;
+       i += nb * kSelThreads) {
+    f32x4 acc = Sj.part[i];
+    for (int s = 1; s < Sj.S; ++s) acc += Sj.part[s * Sj.n4 + i];
+    Sj.out[i] = acc;
+  }
+}
+
+namespace {
+hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj, int sum_blocks,
+                             hipStream_t st) {
   static bool attr_set = false;
-  const size_t lds = (size_t)pool * sizeof(uint32_t);
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_sum_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kMaxPool * (int)sizeof(uint32_t));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(select_kernel, dim3(hkv), dim3(kSelThreads), lds, st, sig_part, rt, ldsig,
-                     pool, budget, scores, ldscores, sel, ldsel);
+  const size_t lds = (size_t)J.pool * sizeof(uint32_t);
+  hipLaunchKernelGGL(select_sum_kernel, dim3(n_select + sum_blocks), dim3(kSelThreads), lds, st,
+                     J, n_select, Sj);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
+                         float* scores, int ldscores, int32_t* sel, int ldsel,
+                         const float* o_part, int S, int64_t o_elems, float* o,
+                         hipStream_t st) {
+  SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, sel, ldsel};
+  SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
+               S};
+  int sum_blocks = 0;
+  if (o_part && S > 1 && o_elems > 0) {
+    const int64_t want = (Sj.n4 + kSelThreads - 1) / kSelThreads;
+    sum_blocks = (int)(want < 1024 ? want : 1024);
+  }
+  return launch_select_sum(J, hkv, Sj, sum_blocks, st);
 }
 
 }  // namespace skv

@@ -57,6 +57,11 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (s > q.max_tiles) s = q.max_tiles;
   if (s < 1) s = 1;
   q.splits = s;
+  // the statistics pass writes only two floats per row and split: with the
+  // automatic choice it takes twice the splits (two workgroups per CU)
+  int ss = cfg->num_splits ? s : 2 * s;
+  if (ss > q.max_tiles) ss = q.max_tiles;
+  q.stat_splits = ss;
   q.ldsig = ceil_div(q.max_pool, kKeyTile) * kKeyTile;
   // full-attention baseline: the pool grows to the whole detailed cache
   int64_t full_tiles = (q.cap + kKeyTile - 1) / kKeyTile;
@@ -67,6 +72,7 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (fs < 1) fs = 1;
   q.full_splits = fs;
   q.part_splits = q.splits > q.full_splits ? q.splits : q.full_splits;
+  if (q.stat_splits > q.part_splits) q.part_splits = q.stat_splits;
 
   const size_t A = 256;
   size_t off = 0;
@@ -80,9 +86,10 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   q.off_dk = off; off = align_up(off + d_rows * D * 2, A);
   q.off_dv = off; off = align_up(off + d_rows * D * 2, A);
   const size_t stat = (size_t)q.part_splits * Hq * q.tpad * 4;
+  const size_t opart = (size_t)(q.splits > q.full_splits ? q.splits : q.full_splits);
   q.off_m = off; off = align_up(off + stat, A);
   q.off_l = off; off = align_up(off + stat, A);
-  q.off_o = off; off = align_up(off + (size_t)q.part_splits * T * Hq * D * 4, A);
+  q.off_o = off; off = align_up(off + opart * T * Hq * D * 4, A);
   q.off_sig = off; off = align_up(off + (size_t)Hkv * q.rt * q.ldsig * 4, A);
   q.off_scores = off; off = align_up(off + (size_t)Hkv * q.ldsig * 4, A);
   q.off_sel = off; off = align_up(off + (size_t)Hkv * B * 4, A);
@@ -94,6 +101,11 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
 int splits_for_pool(const Plan& p, int pool) {
   int tiles = ceil_div(pool, kKeyTile);
   return p.splits < tiles ? p.splits : tiles;
+}
+
+int stat_splits_for_pool(const Plan& p, int pool) {
+  int tiles = ceil_div(pool, kKeyTile);
+  return p.stat_splits < tiles ? p.stat_splits : tiles;
 }
 
 }  // namespace skv

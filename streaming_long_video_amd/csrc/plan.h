@@ -12,9 +12,7 @@ namespace skv {
 
 // Kernel tiling shared by the host plan and the kernels.
 constexpr int kTokBlk = 32;     // query tokens per MFMA block (MFMA n dimension)
-constexpr int kWaves = 4;       // waves per attention workgroup
-constexpr int kQBlkPerWave = 2; // query blocks held by each wave
-constexpr int kRowBlk = kWaves * kQBlkPerWave;  // query blocks per row tile
+constexpr int kRowBlk = 8;      // query blocks per attention row tile (256 rows)
 constexpr int kKeyTile = 64;    // keys staged in LDS per step
 constexpr int kTargetWGs = 256; // one workgroup per compute unit on MI355X
 constexpr int kMaxPool = 32768; // B + T limit (select keeps the pool in LDS)
@@ -33,10 +31,11 @@ struct Plan {
   int32_t tpad;       // ntblk * kTokBlk
   int32_t max_pool;   // B + T
   int32_t max_tiles;  // ceil(max_pool / kKeyTile)
-  int32_t splits;     // key splits of the StateKV attention grid
+  int32_t splits;     // key splits of the StateKV output pass
+  int32_t stat_splits;  // key splits of the StateKV statistics pass
   int32_t ldsig;      // row stride (floats) of score partials / scores
   int32_t full_splits;  // key splits of the full-attention baseline
-  int32_t part_splits;  // max(splits, full_splits): partial buffers sized for it
+  int32_t part_splits;  // largest of the split counts: partial buffers sized for it
   // workspace offsets (bytes, 256-aligned)
   size_t off_ck[2], off_cv[2], off_cpos[2];
   size_t off_dk, off_dv;
@@ -48,7 +47,9 @@ struct Plan {
 // Fills *plan from *cfg.  Returns STATEKV_OK or an error status.
 int make_plan(const statekv_layer_config* cfg, Plan* plan);
 
-// Splits actually used for a pool of `pool` candidates (never more than tiles).
+// Splits actually used for a pool of `pool` candidates (never more than tiles):
+// output pass, and statistics pass.
 int splits_for_pool(const Plan& p, int pool);
+int stat_splits_for_pool(const Plan& p, int pool);
 
 }  // namespace skv

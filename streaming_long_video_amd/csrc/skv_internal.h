@@ -15,15 +15,16 @@ struct AttnArgs {
   const uint16_t* vf;  // [T][Hkv][D] bf16, frame values
   const uint16_t* kc;  // [Hkv][ldc][D] bf16, state keys (rows [0, c) live)
   const uint16_t* vc;  // [Hkv][ldc][D] bf16, state values
-  float* m_part;       // [S][Hq][tpad] per-split row max of raw logits
-  float* l_part;       // [S][Hq][tpad] per-split sum of exp relative to m
+  float* m_part;       // [Sst][Hq][tpad] per-split row max of raw logits
+  float* l_part;       // [Sst][Hq][tpad] per-split sum of exp relative to m
   float* o_out;        // [T][Hq][D] fp32 when S == 1, else [S][T][Hq][D] partials
   float* sig_part;     // [Hkv][rt][ldsig] per-row-tile score partials
   int64_t ldc;         // state rows per KV head (B)
   int T, Hq, Hkv, G;
   int c;               // live state rows; pool = c + T
   int ntblk, nqblk, rt, tpad;
-  int S;               // key splits
+  int S;               // key splits of this launch
+  int Sst;             // splits of the statistics pass (read by the output pass)
   int ldsig;
   float scale_log2;    // softmax scale * log2(e)
   int causal;
@@ -31,14 +32,14 @@ struct AttnArgs {
 
 hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st);
-// o[i] = sum_{s<S} part[s*n + i] (fixed order); n counts floats.
-hipError_t launch_split_sum(const float* part, int S, int64_t n, float* o, hipStream_t st);
-
-// Sums score partials, writes scores, selects the top-B (or keeps all).
-// Standalone mode: rt = 1 and sig_part holds the scores (scores may be null).
+// One launch: per KV head, sums the score partials (scores may be null),
+// selects the top-B or keeps all (sel); concurrently, when o_part is given
+// and S > 1, o[i] = sum_{s<S} o_part[s*o_elems + i] in split order.
+// Standalone mode: rt = 1 and sig_part holds the scores.
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
-                         int budget, float* scores, int ldscores, int32_t* sel,
-                         int ldsel, hipStream_t st);
+                         int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
+                         const float* o_part, int S, int64_t o_elems, float* o,
+                         hipStream_t st);
 
 struct GatherArgs {
   const uint16_t* kc_prev;  // [Hkv][B][D]

@@ -149,19 +149,19 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   float* opart = at<float>(L, p.off_o);
   a.o_out = a.S == 1 ? o : opart;
 
+  a.Sst = skv::stat_splits_for_pool(p, pool);
+  skv::AttnArgs a1 = a;
+  a1.S = a.Sst;
   hipError_t e = timed(L, STATEKV_KERNEL_ATTN_STATS, st,
-                       [&] { return skv::launch_attn_stats(a, p.D, st); });
+                       [&] { return skv::launch_attn_stats(a1, p.D, st); });
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_attn_out(a, p.D, st); });
-  if (e == hipSuccess && a.S > 1)
-    e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st, [&] {
-      return skv::launch_split_sum(opart, a.S, (int64_t)p.T * p.Hq * p.D, o, st);
-    });
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_SELECT, st, [&] {
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
-                                p.B, st);
+                                p.B, a.S > 1 ? opart : nullptr, a.S,
+                                (int64_t)p.T * p.Hq * p.D, o, st);
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
@@ -231,6 +231,7 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   a.c = (int)hist;
   const int tiles = (int)((hist + p.T + skv::kKeyTile - 1) / skv::kKeyTile);
   a.S = p.full_splits < tiles ? p.full_splits : tiles;
+  a.Sst = a.S;
   a.o_out = a.S == 1 ? o : at<float>(L, p.off_o);
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_full_attn(a, p.D, st); });
@@ -371,7 +372,7 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
-                                       budget, st));
+                                       budget, nullptr, 1, 0, nullptr, st));
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@ static void check_layout(const statekv_layer_config& c) {
       {p.off_dk, dr * p.D * 2},     {p.off_dv, dr * p.D * 2},
       {p.off_m, (size_t)p.part_splits * p.Hq * p.tpad * 4},
       {p.off_l, (size_t)p.part_splits * p.Hq * p.tpad * 4},
-      {p.off_o, (size_t)p.part_splits * p.T * p.Hq * p.D * 4},
+      {p.off_o, (size_t)std::max(p.splits, p.full_splits) * p.T * p.Hq * p.D * 4},
       {p.off_sig, (size_t)p.Hkv * p.rt * p.ldsig * 4},
       {p.off_scores, (size_t)p.Hkv * p.ldsig * 4},
       {p.off_sel, (size_t)p.Hkv * p.B * 4}};
@@ -56,9 +56,13 @@ static void check_layout(const statekv_layer_config& c) {
   CHECK(p.ldsig >= p.B + p.T && p.ldsig % skv::kKeyTile == 0);
   CHECK(p.splits >= 1 && p.splits <= p.max_tiles);
   CHECK(p.Hkv * p.rt * p.splits <= skv::kTargetWGs || p.splits == 1);
+  CHECK(p.stat_splits >= p.splits && p.stat_splits <= p.max_tiles);
+  CHECK(p.part_splits >= p.stat_splits && p.part_splits >= p.full_splits);
   for (int pool = 1; pool <= p.B + p.T; pool += 97) {
     const int s = skv::splits_for_pool(p, pool);
     CHECK(s >= 1 && s <= (pool + skv::kKeyTile - 1) / skv::kKeyTile);
+    const int s1 = skv::stat_splits_for_pool(p, pool);
+    CHECK(s1 >= s && s1 <= (pool + skv::kKeyTile - 1) / skv::kKeyTile);
   }
 }
 
@@ -71,7 +75,7 @@ int main() {
   check_layout(cfg(16, 1, 64, 4096, 28672, 4096));
   skv::Plan p;
   statekv_layer_config c = cfg(28, 4, 128, 256, 4096, 131072);
-  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.rt == 7);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.stat_splits == 18 && p.rt == 7);
   c = cfg(28, 4, 96, 256, 4096, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
   c = cfg(28, 5, 128, 256, 4096, 131072);
@@ -91,7 +95,7 @@ int main() {
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
   c.flags = 0;
   c.num_splits = 3;
-  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 3);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 3 && p.stat_splits == 3);
   CHECK(skv::make_plan(nullptr, &p) == STATEKV_ERR_INVALID_ARGUMENT);
   if (failures) return 1;
   printf("plan checks passed\n");
