@@ -10,10 +10,12 @@ state: 16*256 = B) and K=496 timed frames, i.e. the pages' 512-frame stream.
 All frames are generated on the host (seeded, synthetic) and staged in HBM
 before the timed region.
 
-Prints ONE JSON line: frames/s per layer, a roofline entry for the dominant
-kernel (its average launch time measured with HIP events on the launch
-stream during the timed region), the per-kernel breakdown and the float64
-CPU oracle timed on a bounded sample of the same stream.
+Prints ONE JSON line: frames/s per layer over the K timed frames (no
+per-launch instrumentation inside them), a roofline entry for the dominant
+kernel and the per-kernel breakdown (launch durations from HIP events that the
+dispatch itself timestamps on the launch stream, over the 32 frames right
+after the timed region, state still full), and the float64 CPU oracle timed
+on a bounded sample of the same stream.
 
 Other measurements (not the headline line):
     --mode crossover   StateKV vs quadratic full attention, 1B shape,
@@ -25,7 +27,6 @@ Other measurements (not the headline line):
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -40,6 +41,7 @@ import numpy as np  # noqa: E402
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "internvl3_8b_layer"
+DOMINANT = "attn_out"        # the longest kernel of the step (attention pass 2)
 
 
 def _fail_multi_gpu(n):
@@ -124,23 +126,19 @@ def cpu_baseline(spec, qs, ks, vs, warm: int, budget_s: float):
 # traffic counters taken with rocprofv3 (committed under profiles/)
 # ----------------------------------------------------------------------------
 
-def _kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in ("streaming_long_video_amd/csrc/kernels/attention.hip",):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    from streaming_long_video_amd.profiling import source_hash
+
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(kernel)
-    if not entry or entry.get("source_hash") != _kernel_source_hash():
+    entry = data.get("kernels", {}).get(kernel)
+    if not entry or data.get("source_hash") != source_hash():
         return None
     return entry.get("bytes_per_launch")
 
@@ -159,7 +157,8 @@ def run_headline(args):
     if spec.n_layers != 1:
         raise SystemExit("the headline mode runs single-layer workloads")
     W, K = args.warmup, args.steps
-    N = W + K
+    KB = args.breakdown_steps  # extra frames after the timed region, every kernel timed
+    N = W + K + KB
     T, Hq, Hkv, d, Bs = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
                          spec.state_budget)
     t_gen = time.perf_counter()
@@ -177,9 +176,20 @@ def run_headline(args):
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
     for n in range(W):
         layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+    if args.copy_probe_mib > 0:
+        # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # counters scale the kernels' counters to bytes (outside the timed region)
+        n_el = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n_el, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        del src, dst
     torch.cuda.synchronize()
 
-    mask = {"none": 0, "dominant": 1 << 1, "all": (1 << len(skv.STATEKV_KERNELS)) - 1}[args.events]
+    all_mask = (1 << len(skv.STATEKV_KERNELS)) - 1
+    mask = {"none": 0, "dominant": 1 << skv.STATEKV_KERNELS.index(DOMINANT),
+            "all": all_mask}[args.events]
     skv.statekv_profile_start(layer.handle, mask, K * len(skv.STATEKV_KERNELS))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -189,11 +199,22 @@ def run_headline(args):
     elapsed = time.perf_counter() - t0
     prof = skv.statekv_profile_stop(layer.handle)
 
-    cs = [min(Bs, n * T) for n in range(W, N)]
-    c_mean = float(np.mean(cs))
+    # per-kernel breakdown on the frames after the timed region (events around
+    # every launch cost a little time, so they stay out of the timed frames)
     kernels_us = {k: (ms / cnt * 1e3 if cnt else None) for k, (ms, cnt) in prof.items()}
-    timed_kernels = {k: v for k, v in kernels_us.items() if v}
-    dominant = max(timed_kernels, key=timed_kernels.get) if timed_kernels else "attn_out"
+    if KB > 0:
+        skv.statekv_profile_start(layer.handle, all_mask, KB * len(skv.STATEKV_KERNELS))
+        for i in range(KB):
+            n = W + K + i
+            layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+        torch.cuda.synchronize()
+        bd = skv.statekv_profile_stop(layer.handle)
+        breakdown_us = {k: ms / cnt * 1e3 for k, (ms, cnt) in bd.items() if cnt}
+    else:
+        breakdown_us = {k: v for k, v in kernels_us.items() if v}
+
+    cs = [min(Bs, n * T) for n in range(W, W + K)]
+    dominant = DOMINANT
     flops = float(np.mean([attn_out_flops(Hq, d, T, c) for c in cs]))
     result = {
         "metric": "video-prefill frames/s per layer + % bf16 MFMA peak (8B shape, B=4096, T=256)",
@@ -213,7 +234,12 @@ def run_headline(args):
                    "head_dim": d, "frame_tokens": T, "state_budget": Bs,
                    "frames": N, "detailed_capacity": N * T},
     }
-    att = kernels_us.get("attn_out")
+    # the dominant kernel's launch duration: HIP events timestamped by the
+    # dispatch on the launch stream -- from the timed region when it was
+    # instrumented, else from the breakdown frames that follow it
+    att = kernels_us.get("attn_out") or breakdown_us.get("attn_out")
+    att_src = ("timed region" if kernels_us.get("attn_out") else
+               f"frames {W + K}..{W + K + KB - 1}, right after the timed region")
     if att:
         achieved = flops / (att * 1e-6) / 1e12
         result["roofline"] = {
@@ -222,23 +248,26 @@ def run_headline(args):
             "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
             "traffic": measured_traffic("attn_out"),
             "flops_per_launch": flops, "avg_launch_us": att,
+            "avg_launch_us_from": "HIP events on the launch stream, " + att_src,
         }
-    if kernels_us.get("attn_stats") and att:
+    if breakdown_us.get("attn_stats") and breakdown_us.get("attn_out"):
         useful = float(np.mean([useful_attention_flops(Hq, d, T, c) for c in cs]))
-        t_att = (kernels_us["attn_stats"] + att + (kernels_us.get("split_sum") or 0.0)) * 1e-6
+        t_att = (breakdown_us["attn_stats"] + breakdown_us["attn_out"]) * 1e-6
         result["attention"] = {
             "useful_tflops": useful / t_att / 1e12,
             "useful_frac_of_peak": useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
             "executed_frac_of_peak": 1.5 * useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
         }
-    if kernels_us.get("gather"):
+    if breakdown_us.get("gather"):
         gb = float(np.mean([gather_bytes(Hkv, d, T, Bs, c) for c in cs]))
+        tg = breakdown_us["gather"]
         result["gather_append"] = {
-            "bytes_per_launch": gb, "avg_launch_us": kernels_us["gather"],
-            "achieved_gbs": gb / (kernels_us["gather"] * 1e-6) / 1e9,
-            "frac_of_hbm_peak": gb / (kernels_us["gather"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "bytes_per_launch": gb, "avg_launch_us": tg,
+            "achieved_gbs": gb / (tg * 1e-6) / 1e9,
+            "frac_of_hbm_peak": gb / (tg * 1e-6) / 1e9 / PEAK_HBM_GBS,
         }
-    result["kernels_us"] = kernels_us
+    result["kernels_us"] = {k: v for k, v in breakdown_us.items()}
+    result["kernels_us_frames"] = f"{W + K}..{W + K + KB - 1}" if KB > 0 else "timed frames"
     result["dominant_kernel"] = dominant
     result["event_mode"] = args.events
     result["input_generation_s"] = t_gen
@@ -357,8 +386,14 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--mode", choices=["headline", "crossover", "depth28"], default="headline")
-    ap.add_argument("--events", choices=["none", "dominant", "all"], default="all",
-                    help="kernels bracketed by HIP events during the timed region")
+    ap.add_argument("--events", choices=["none", "dominant", "all"], default="none",
+                    help="kernels timed with HIP events during the timed region (each timed "
+                         "launch costs a few microseconds of dispatch serialisation)")
+    ap.add_argument("--breakdown-steps", type=int, default=32,
+                    help="frames after the timed region with every kernel timed")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain device copy of this size before the timed region "
+                         "(reference kernel for rocprofv3 byte counters)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -54,6 +54,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;        // two waves per SIMD
 constexpr int kQBlkPerWave = 1;  // 32-token query blocks per wave
 constexpr int kThreads = kWaves * 64;
+
+// Keeps the compiler's scheduler from moving instructions across phase
+// boundaries of the block step (operand reads / softmax / MFMA issue).
+#define SKV_FENCE() __builtin_amdgcn_sched_barrier(0)
 constexpr int kKPad = 8;  // bf16 padding per K row in LDS (conflict-free b128 reads)
 constexpr int kVPad = 4;  // fp16 padding per V^T row (conflict-free b64 reads)
 constexpr float kPUnscale = 1.f / 4096.f;  // P is formed as 2^12 * P
@@ -164,6 +168,27 @@ struct TileStage {
     }
   }
 
+  // Tile wholly inside the state: no per-chunk source choice, no bounds.
+  __device__ inline void load_state(const AttnArgs& a, int h, int key0, int tid) {
+    const uint16_t* kb = a.kc + ((int64_t)h * a.ldc + key0) * D;
+    const uint16_t* vb = a.vc + ((int64_t)h * a.ldc + key0) * D;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      k[i] = *reinterpret_cast<const u32x4*>(kb + ch * 8);
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + i * kThreads;
+        if (VPART && it >= VITEMS) continue;
+        const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
+        v0[i] = *reinterpret_cast<const u32x4*>(vb + (2 * kp) * D + dc);
+        v1[i] = *reinterpret_cast<const u32x4*>(vb + (2 * kp + 1) * D + dc);
+      }
+    }
+  }
+
   // K rows as they are; V transposed to [d][key] and converted to fp16.
   __device__ inline void store(uint16_t* Ks, _Float16* Vt, int tid) const {
     constexpr int KLD = D + kKPad, VLD = kKeyTile + kVPad;
@@ -240,6 +265,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int wg_klim = a.causal ? c + wg_tmax + 1 : pool;
   const int tile_end = max(tile_lo, min(tile_hi, (wg_klim + KT - 1) / KT));
 
+  // the first key tile's global loads go out first, so that their latency
+  // overlaps the Q and row-statistics loads below
+  TileStage<D, WITH_V> stage;
+  auto stage_load = [&](int key0) __attribute__((always_inline)) {
+    if (key0 + KT <= c) stage.load_state(a, h, key0, tid);
+    else stage.load(a, h, pool, key0, tid);
+  };
+  if (tile_end > tile_lo) stage_load(tile_lo * KT);
+
   bf16x8 qreg[QB][NKK];
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
@@ -268,64 +302,110 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] = f32x16{};
   }
   if constexpr (PASS == 2) {
-    // Row log-sum-exp (base 2, scaled logits) from the split statistics,
-    // combined in split order; 12 is subtracted so that P comes out * 2^12.
+    // Row log-sum-exp (base 2, scaled logits) of the row tile's 256 rows from
+    // the statistics pass's per-split (max, sum) pairs.  Thread pair
+    // (r, r + 256) takes row r, each half of the splits (even / odd index),
+    // every load of a group in flight at once; the halves merge through LDS.
+    // 12 is subtracted so that P comes out * 2^12.
+    {
+      static_assert(kThreads == 2 * kRowBlk * kTokBlk, "two threads per row");
+      constexpr int kGrp = 16;
+      __shared__ float mh[2][kRowBlk * kTokBlk], lh[2][kRowBlk * kTokBlk];
+      const int r = tid % (kRowBlk * kTokBlk), par = tid / (kRowBlk * kTokBlk);
+      const int b = b0 + r / kTokBlk;
+      const int t = (b / a.G) * kTokBlk + r % kTokBlk;
+      float M = -INFINITY, L = 0.f;
+      if (b < a.nqblk && t < a.T) {
+        const int64_t stride = (int64_t)a.Hq * a.tpad;
+        const float* mp = a.m_part + (int64_t)(h * a.G + b % a.G) * a.tpad + t;
+        const float* lp = a.l_part + (int64_t)(h * a.G + b % a.G) * a.tpad + t;
+        for (int s0 = par; s0 < a.Sst; s0 += 2 * kGrp) {
+          float mv[kGrp], lv[kGrp];
 #pragma unroll
-    for (int i = 0; i < QB; ++i) {
-      if (qtok[i] < 0) continue;
-      const int64_t row = (int64_t)qhead[i] * a.tpad + qtok[i];
-      const int64_t stride = (int64_t)a.Hq * a.tpad;
-      float M = -INFINITY;
-      for (int sp = 0; sp < a.Sst; ++sp) M = fmaxf(M, a.m_part[sp * stride + row]);
-      float L = 0.f;
-      for (int sp = 0; sp < a.Sst; ++sp) {
-        const float ms = a.m_part[sp * stride + row];
-        if (ms > -INFINITY) L += a.l_part[sp * stride + row] * exp2f((ms - M) * sl2);
+          for (int u = 0; u < kGrp; ++u) {
+            const int sp = s0 + 2 * u;
+            const bool in = sp < a.Sst;
+            mv[u] = in ? mp[sp * stride] : -INFINITY;
+            lv[u] = in ? lp[sp * stride] : 0.f;
+          }
+          float Mg = M;
+#pragma unroll
+          for (int u = 0; u < kGrp; ++u) Mg = fmaxf(Mg, mv[u]);
+          const float Ms = Mg == -INFINITY ? 0.f : Mg;
+          L = M == -INFINITY ? 0.f : L * exp2f((M - Ms) * sl2);
+#pragma unroll
+          for (int u = 0; u < kGrp; ++u)
+            if (mv[u] > -INFINITY) L += lv[u] * exp2f((mv[u] - Ms) * sl2);
+          M = Mg;
+        }
       }
-      lse2[i] = M * sl2 + log2f(L) - 12.f;
+      mh[par][r] = M;
+      lh[par][r] = L;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < QB; ++i) {
+        if (qtok[i] < 0) continue;
+        const int rr = (w * QB + i) * kTokBlk + l32;
+        const float m0 = mh[0][rr], m1 = mh[1][rr];
+        const float Mx = fmaxf(m0, m1);
+        float Lx = 0.f;
+        if (m0 > -INFINITY) Lx += lh[0][rr] * exp2f((m0 - Mx) * sl2);
+        if (m1 > -INFINITY) Lx += lh[1][rr] * exp2f((m1 - Mx) * sl2);
+        lse2[i] = Mx * sl2 + log2f(Lx) - 12.f;
+      }
     }
   }
 
   // -- per-32-key-block work -----------------------------------------------
   // register r of query block i holds frame offset kbase - c + 8(r/4) + 4 half
   // + r%4 of its key, visible iff that offset does not exceed qlim[i]
-  auto visible = [&](int kbase, int i, int r) {
+  auto visible = [&](int kbase, int i, int r) __attribute__((always_inline)) {
     return 8 * (r >> 2) + (r & 3) <= qlim[i] - (kbase - c + 4 * half);
   };
 
-  auto qk_block = [&](const uint16_t* K, int kb, f32x16 (&sacc)[QB]) {
+  // K rows of block kb as the A operand of S^T = K Q^T: 8 consecutive d per
+  // lane, one 16-wide d step per fragment
+  auto read_k = [&](const uint16_t* K, int kb, bf16x8 (&kf)[NKK]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + l32) * KLD + kk * 16 + half * 8]);
+  };
+  auto mfma_qk = [&](const bf16x8 (&kf)[NKK], f32x16 (&sacc)[QB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < QB; ++i) sacc[i] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const bf16x8 ak =
-          *reinterpret_cast<const bf16x8*>(&K[(kb * 32 + l32) * KLD + kk * 16 + half * 8]);
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
       for (int i = 0; i < QB; ++i)
-        sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qreg[i][kk], sacc[i], 0, 0, 0);
-    }
+        sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[i][kk], sacc[i], 0, 0, 0);
   };
-
-  auto pv_block = [&](const _Float16* V, int kb, const u32x4 (&ph)[QB][2]) {
+  // V^T rows (d) of block kb as the A operand of O^T = V^T P^T, key slots in
+  // the order of the logits' registers (8(r/4) + 4 half + r%4)
+  auto read_v = [&](const _Float16* V, int kb, u32x4 (&vf)[NMB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int slab = 0; slab < 2; ++slab) {
         const _Float16* vrow = &V[(mb * 32 + l32) * VLD + kb * 32 + slab * 16 + 4 * half];
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+        vf[mb][slab] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+  };
+  auto mfma_pv = [&](const u32x4 (&vf)[NMB][2], const u32x4 (&ph)[QB][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int slab = 0; slab < 2; ++slab)
 #pragma unroll
         for (int i = 0; i < QB; ++i)
           oacc[i][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, ph[i][slab]),
+              __builtin_bit_cast(f16x8, vf[mb][slab]), __builtin_bit_cast(f16x8, ph[i][slab]),
               oacc[i][mb], 0, 0, 0);
-      }
-    }
   };
 
   // pass 1: online row max / sum of exp over this block
-  auto stats_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked) {
+  auto stats_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
       float z[16];
@@ -354,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
   // pass 2: normalised P (x 2^12) -> fp16 pairs, column sums -> LDS
   auto scores_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked, int kb,
-                          float* sw, u32x4 (&ph)[QB][2]) {
+                          float* sw, u32x4 (&ph)[QB][2]) __attribute__((always_inline)) {
     float p[QB][16];
 #pragma unroll
     for (int i = 0; i < QB; ++i)
@@ -386,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
   // pass 3: online softmax with rescaled O (quadratic baseline)
   auto online_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked,
-                          u32x4 (&ph)[QB][2]) {
+                          u32x4 (&ph)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
       float z[16];
@@ -421,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
   };
 
-  auto emit_scores = [&](int tile, const float* sw) {
+  auto emit_scores = [&](int tile, const float* sw) __attribute__((always_inline)) {
     if constexpr (PASS == 2) {
       if (tid < KT) {
         const int j = tile * KT + tid;
@@ -436,9 +516,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   };
 
   // -- the tile loop (double-buffered LDS, one barrier per tile) -------------
-  TileStage<D, WITH_V> stage;
   if (tile_end > tile_lo) {
-    stage.load(a, h, pool, tile_lo * KT, tid);
     stage.store(Ks[0], Vt[0], tid);
     __syncthreads();
   }
@@ -446,10 +524,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const int cur = (tile - tile_lo) & 1;
     const int key0 = tile * KT;
     const bool more = tile + 1 < tile_end;
-    if (more) stage.load(a, h, pool, key0 + KT, tid);
+    if (more) stage_load(key0 + KT);
     if constexpr (PASS == 2) {
       if (tile > tile_lo) emit_scores(tile - 1, sigw[cur ^ 1]);
     }
+    bf16x8 kf[NKK];
+    read_k(Ks[cur], 0, kf);
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
       const int kbase = key0 + kb * 32;
@@ -457,20 +537,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       // pool) are fully visible to every query
       const bool masked = a.causal ? (kbase + 32 > c) : (kbase + 32 > pool);
       f32x16 sacc[QB];
-      qk_block(Ks[cur], kb, sacc);
+      mfma_qk(kf, sacc);
       if constexpr (PASS == 1) {
+        if (kb + 1 < KT / 32) read_k(Ks[cur], kb + 1, kf);
+        SKV_FENCE();
         if (masked) stats_block(sacc, kbase, true);
         else stats_block(sacc, kbase, false);
-      } else if constexpr (PASS == 2) {
-        u32x4 ph[QB][2];
-        if (masked) scores_block(sacc, kbase, true, kb, sigw[cur], ph);
-        else scores_block(sacc, kbase, false, kb, sigw[cur], ph);
-        pv_block(Vt[cur], kb, ph);
       } else {
+        u32x4 vf[NMB][2];
+        read_v(Vt[cur], kb, vf);
+        SKV_FENCE();
         u32x4 ph[QB][2];
-        if (masked) online_block(sacc, kbase, true, ph);
-        else online_block(sacc, kbase, false, ph);
-        pv_block(Vt[cur], kb, ph);
+        if constexpr (PASS == 2) {
+          if (masked) scores_block(sacc, kbase, true, kb, sigw[cur], ph);
+          else scores_block(sacc, kbase, false, kb, sigw[cur], ph);
+        } else {
+          if (masked) online_block(sacc, kbase, true, ph);
+          else online_block(sacc, kbase, false, ph);
+        }
+        SKV_FENCE();
+        mfma_pv(vf, ph);
+        if (kb + 1 < KT / 32) read_k(Ks[cur], kb + 1, kf);
+        SKV_FENCE();
       }
     }
     if (more) stage.store(Ks[cur ^ 1], Vt[WITH_V ? cur ^ 1 : 0], tid);
@@ -571,35 +659,35 @@ namespace {
 int attn_grid(const AttnArgs& a) { return a.Hkv * a.S * a.rt; }
 
 template <int PASS>
-hipError_t launch_pass(const AttnArgs& a, int D, hipStream_t st) {
+hipError_t launch_pass(const AttnArgs& a, int D, const Stream& st) {
   if (D == 128)
-    hipLaunchKernelGGL((attn_kernel<128, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
+    hipExtLaunchKernelGGL((attn_kernel<128, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st.st, st.start, st.stop, 0, a);
   else
-    hipLaunchKernelGGL((attn_kernel<64, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st, a);
+    hipExtLaunchKernelGGL((attn_kernel<64, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st.st, st.start, st.stop, 0, a);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st) {
+hipError_t launch_attn_stats(const AttnArgs& a, int D, const Stream& st) {
   return launch_pass<1>(a, D, st);
 }
 
-hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st) {
+hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st) {
   return launch_pass<2>(a, D, st);
 }
 
-hipError_t launch_full_attn(const AttnArgs& a, int D, hipStream_t st) {
+hipError_t launch_full_attn(const AttnArgs& a, int D, const Stream& st) {
   return launch_pass<3>(a, D, st);
 }
 
-hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, hipStream_t st) {
+hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st) {
   const int64_t n4 = (int64_t)a.T * a.Hq * (D / 4);
   int64_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (D == 128)
-    hipLaunchKernelGGL((full_combine_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st, a, o);
+    hipExtLaunchKernelGGL((full_combine_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, st.st, st.start, st.stop, 0, a, o);
   else
-    hipLaunchKernelGGL((full_combine_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st, a, o);
+    hipExtLaunchKernelGGL((full_combine_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, st.st, st.start, st.stop, 0, a, o);
   return hipGetLastError();
 }
 

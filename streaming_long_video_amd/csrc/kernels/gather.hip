@@ -97,26 +97,26 @@ __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs 
 
 namespace {
 hipError_t launch(const GatherArgs& g, int D, int gather_blocks, int append_blocks,
-                  hipStream_t st) {
+                  const Stream& st) {
   const int blocks = gather_blocks + append_blocks;
   if (blocks == 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL((gather_append_kernel<128>), dim3(blocks), dim3(kCopyThreads), 0, st, g,
+    hipExtLaunchKernelGGL((gather_append_kernel<128>), dim3(blocks), dim3(kCopyThreads), 0, st.st, st.start, st.stop, 0, g,
                        gather_blocks);
   else
-    hipLaunchKernelGGL((gather_append_kernel<64>), dim3(blocks), dim3(kCopyThreads), 0, st, g,
+    hipExtLaunchKernelGGL((gather_append_kernel<64>), dim3(blocks), dim3(kCopyThreads), 0, st.st, st.start, st.stop, 0, g,
                        gather_blocks);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_gather_append(const GatherArgs& g, int D, hipStream_t st) {
+hipError_t launch_gather_append(const GatherArgs& g, int D, const Stream& st) {
   const int gather_blocks = g.Hkv * ((g.newc + kRowsPerBlock - 1) / kRowsPerBlock);
   const int append_blocks = g.kd ? g.Hkv * ((g.T + kRowsPerBlock - 1) / kRowsPerBlock) : 0;
   return launch(g, D, gather_blocks, append_blocks, st);
 }
 
-hipError_t launch_append_only(const GatherArgs& g, int D, hipStream_t st) {
+hipError_t launch_append_only(const GatherArgs& g, int D, const Stream& st) {
   return launch(g, D, 0, g.Hkv * ((g.T + kRowsPerBlock - 1) / kRowsPerBlock), st);
 }
 

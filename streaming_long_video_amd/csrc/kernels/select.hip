@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
 
 namespace {
 hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj, int sum_blocks,
-                             hipStream_t st) {
+                             const Stream& st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_sum_kernel),
@@ -236,7 +236,7 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj,
     attr_set = true;
   }
   const size_t lds = (size_t)J.pool * sizeof(uint32_t);
-  hipLaunchKernelGGL(select_sum_kernel, dim3(n_select + sum_blocks), dim3(kSelThreads), lds, st,
+  hipExtLaunchKernelGGL(select_sum_kernel, dim3(n_select + sum_blocks), dim3(kSelThreads), lds, st.st, st.start, st.stop, 0,
                      J, n_select, Sj);
   return hipGetLastError();
 }
@@ -245,7 +245,7 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj,
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o,
-                         hipStream_t st) {
+                         const Stream& st) {
   SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, sel, ldsel};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};

@@ -2,11 +2,21 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "plan.h"
 
 namespace skv {
+
+// A launch's stream and, when set, two events that the dispatch itself
+// timestamps at the kernel's start and end (hipExtLaunchKernel).
+struct Stream {
+  hipStream_t st;
+  hipEvent_t start = nullptr, stop = nullptr;
+  Stream(hipStream_t s) : st(s) {}  // NOLINT: plain streams convert implicitly
+  Stream(hipStream_t s, hipEvent_t a, hipEvent_t b) : st(s), start(a), stop(b) {}
+};
 
 // Arguments of the two attention passes over the pool [C_{n-1} ; frame].
 struct AttnArgs {
@@ -30,8 +40,8 @@ struct AttnArgs {
   int causal;
 };
 
-hipError_t launch_attn_stats(const AttnArgs& a, int D, hipStream_t st);
-hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_attn_stats(const AttnArgs& a, int D, const Stream& st);
+hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
 // One launch: per KV head, sums the score partials (scores may be null),
 // selects the top-B or keeps all (sel); concurrently, when o_part is given
 // and S > 1, o[i] = sum_{s<S} o_part[s*o_elems + i] in split order.
@@ -39,7 +49,7 @@ hipError_t launch_attn_out(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
                          int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o,
-                         hipStream_t st);
+                         const Stream& st);
 
 struct GatherArgs {
   const uint16_t* kc_prev;  // [Hkv][B][D]
@@ -60,14 +70,14 @@ struct GatherArgs {
   int keep_all;             // pool <= B: C_n = [C_{n-1} ; frame]
   int ring;
 };
-hipError_t launch_gather_append(const GatherArgs& g, int D, hipStream_t st);
-hipError_t launch_append_only(const GatherArgs& g, int D, hipStream_t st);
+hipError_t launch_gather_append(const GatherArgs& g, int D, const Stream& st);
+hipError_t launch_append_only(const GatherArgs& g, int D, const Stream& st);
 
 // Full-attention baseline (single online-softmax pass): the pool is
 // [D[0:c) ; frame], causal within the frame.  With S == 1 it writes the
 // normalised O to o_out; otherwise unnormalised partials plus (m, l).
-hipError_t launch_full_attn(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_full_attn(const AttnArgs& a, int D, const Stream& st);
 // Combines the unnormalised split partials of the full-attention baseline.
-hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, hipStream_t st);
+hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st);
 
 }  // namespace skv

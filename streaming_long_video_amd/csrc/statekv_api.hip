@@ -70,19 +70,16 @@ skv::AttnArgs attn_args(const statekv_layer* L, const void* q, const void* k, co
 
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
 
-// Runs one kernel launch, bracketed by timing events when the hook asks for it.
+// Runs one kernel launch; when the timing hook asks for it, the dispatch
+// itself timestamps two events at the kernel's start and end.
 template <class F>
 hipError_t timed(statekv_layer* L, int kernel, hipStream_t st, F&& launch) {
-  ProfRecord* r = nullptr;
   if ((L->prof_mask >> kernel) & 1u && L->prof_used < L->prof.size()) {
-    r = &L->prof[L->prof_used++];
+    ProfRecord* r = &L->prof[L->prof_used++];
     r->kernel = kernel;
-    hipError_t e = hipEventRecord(r->before, st);
-    if (e != hipSuccess) return e;
+    return launch(skv::Stream(st, r->before, r->after));
   }
-  hipError_t e = launch();
-  if (r && e == hipSuccess) e = hipEventRecord(r->after, st);
-  return e;
+  return launch(skv::Stream(st));
 }
 
 }  // namespace
@@ -153,15 +150,15 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   skv::AttnArgs a1 = a;
   a1.S = a.Sst;
   hipError_t e = timed(L, STATEKV_KERNEL_ATTN_STATS, st,
-                       [&] { return skv::launch_attn_stats(a1, p.D, st); });
+                       [&](const skv::Stream& ks) { return skv::launch_attn_stats(a1, p.D, ks); });
   if (e == hipSuccess)
-    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_attn_out(a, p.D, st); });
+    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&](const skv::Stream& ks) { return skv::launch_attn_out(a, p.D, ks); });
   if (e == hipSuccess)
-    e = timed(L, STATEKV_KERNEL_SELECT, st, [&] {
+    e = timed(L, STATEKV_KERNEL_SELECT, st, [&](const skv::Stream& ks) {
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
                                 p.B, a.S > 1 ? opart : nullptr, a.S,
-                                (int64_t)p.T * p.Hq * p.D, o, st);
+                                (int64_t)p.T * p.Hq * p.D, o, ks);
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
@@ -186,7 +183,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.newc = newc;
     g.keep_all = pool <= p.B;
     g.ring = ring;
-    e = timed(L, STATEKV_KERNEL_GATHER, st, [&] { return skv::launch_gather_append(g, p.D, st); });
+    e = timed(L, STATEKV_KERNEL_GATHER, st, [&](const skv::Stream& ks) { return skv::launch_gather_append(g, p.D, ks); });
   }
   if (e != hipSuccess) return hip_status(e);
   L->cur = nxt;
@@ -222,7 +219,7 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   g.T = p.T;
   g.Hkv = p.Hkv;
   hipError_t e =
-      timed(L, STATEKV_KERNEL_GATHER, st, [&] { return skv::launch_append_only(g, p.D, st); });
+      timed(L, STATEKV_KERNEL_GATHER, st, [&](const skv::Stream& ks) { return skv::launch_append_only(g, p.D, ks); });
 
   skv::AttnArgs a = attn_args(L, q, k, v);
   a.kc = at<uint16_t>(L, p.off_dk);
@@ -234,10 +231,10 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   a.Sst = a.S;
   a.o_out = a.S == 1 ? o : at<float>(L, p.off_o);
   if (e == hipSuccess)
-    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&] { return skv::launch_full_attn(a, p.D, st); });
+    e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&](const skv::Stream& ks) { return skv::launch_full_attn(a, p.D, ks); });
   if (e == hipSuccess && a.S > 1)
     e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st,
-              [&] { return skv::launch_full_combine(a, o, p.D, st); });
+              [&](const skv::Stream& ks) { return skv::launch_full_combine(a, o, p.D, ks); });
   if (e != hipSuccess) return hip_status(e);
   L->n += 1;
   return STATEKV_OK;
