@@ -23,6 +23,7 @@ namespace skv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+static_assert(kMaxPool / kSelWaves < 65536, "16-bit per-wave histogram counters");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -95,34 +96,41 @@ struct SumJob {
 
 __device__ void select_one_head(const SelectJob& J, int h) {
   extern __shared__ uint32_t keys[];
-  __shared__ uint32_t whist[kSelWaves][256];
+  // per-wave digit histograms, two 16-bit counters per word (a wave sees at
+  // most kMaxPool / kSelWaves = 2048 keys)
+  __shared__ uint32_t whist[2][kSelWaves][128];
   __shared__ uint32_t red[2 * kSelWaves];
-  __shared__ uint32_t found[3];
+  __shared__ uint32_t wtot[4];
+  __shared__ uint32_t found[2][3];
   const int tid = threadIdx.x, w = tid >> 6;
   const int pool = J.pool, budget = J.budget;
   const float* sp = J.sig_part + (int64_t)h * J.rt * J.ldsig;
   int32_t* out = J.sel + (int64_t)h * J.ldsel;
 
   // importance = sum of the row tiles' partial column sums, in tile order;
-  // kLoad candidates per thread per round, all their partials loaded first
-  constexpr int kLoad = 4;
+  // every load of a batch (kLoad candidates x kRows row tiles per thread) is
+  // in flight at once
+  constexpr int kLoad = 5;  // 5 * 1024 >= 4352: one round at the 8B-like shape
+  constexpr int kRows = 4;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int j0 = 0; j0 < pool; j0 += kLoad * kSelThreads) {
     float acc[kLoad];
 #pragma unroll
-    for (int q = 0; q < kLoad; ++q) {
-      const int j = min(j0 + tid + q * kSelThreads, pool - 1);
-      acc[q] = sp[j];
-    }
-    for (int r = 1; r < J.rt; ++r) {
-      float part[kLoad];
+    for (int q = 0; q < kLoad; ++q) acc[q] = 0.f;
+    for (int r0 = 0; r0 < J.rt; r0 += kRows) {
+      float part[kRows][kLoad];
 #pragma unroll
-      for (int q = 0; q < kLoad; ++q) {
-        const int j = min(j0 + tid + q * kSelThreads, pool - 1);
-        part[q] = sp[(int64_t)r * J.ldsig + j];
-      }
+      for (int u = 0; u < kRows; ++u)
 #pragma unroll
-      for (int q = 0; q < kLoad; ++q) acc[q] += part[q];
+        for (int q = 0; q < kLoad; ++q) {
+          const int j = min(j0 + tid + q * kSelThreads, pool - 1);
+          part[u][q] = r0 + u < J.rt ? sp[(int64_t)(r0 + u) * J.ldsig + j] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < kRows; ++u)
+#pragma unroll
+        for (int q = 0; q < kLoad; ++q)
+          if (r0 + u < J.rt) acc[q] = r0 + u == 0 ? part[u][q] : acc[q] + part[u][q];
     }
 #pragma unroll
     for (int q = 0; q < kLoad; ++q) {
@@ -140,10 +148,14 @@ __device__ void select_one_head(const SelectJob& J, int h) {
     for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
     return;
   }
+  // the first pass's histogram starts cleared (the min/max barrier orders it)
+  for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[0][0][0])[i] = 0u;
   uint32_t kmax;
   const uint32_t kmin = block_min_max(mn, mx, red, &kmax);  // also orders keys[] writes
 
-  // radix select below the common prefix of all keys
+  // radix select below the common prefix of all keys; histograms and the
+  // boundary record alternate between two buffers so that a pass needs
+  // three barriers
   uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
   uint32_t k = (uint32_t)budget;  // rank (from the top) still to place
   int hb = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
@@ -151,36 +163,54 @@ __device__ void select_one_head(const SelectJob& J, int h) {
     pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
     prefix = kmin & pmask;
   }
+  int buf = 0;
+  const int lane = tid & 63;
   while (hb >= 0) {
     const int shift = hb >= 7 ? hb - 7 : 0;
     const uint32_t dmask = (2u << (hb - shift)) - 1u;  // digit bits [shift, hb]
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&whist[0][0])[i] = 0u;
-    __syncthreads();
     for (int j = tid; j < pool; j += kSelThreads) {
       const uint32_t u = keys[j];
-      if ((u & pmask) == prefix) atomicAdd(&whist[w][(u >> shift) & dmask], 1u);
+      if ((u & pmask) == prefix) {
+        const uint32_t dig = (u >> shift) & dmask;
+        atomicAdd(&whist[buf][w][dig >> 1], 1u << ((dig & 1u) * 16u));
+      }
     }
+    for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[buf ^ 1][0][0])[i] = 0u;
     __syncthreads();
-    const uint32_t d = 255u - (uint32_t)tid;  // descending digits (tid < 256)
-    uint32_t cnt = 0;
-    if (tid < 256 && d <= dmask) {
+    // digits in descending order over threads 0..255 (waves 0..3)
+    const uint32_t d = 255u - (uint32_t)tid;
+    uint32_t cnt = 0, incl = 0;
+    if (tid < 256) {
+      if (d <= dmask) {
 #pragma unroll
-      for (int i = 0; i < kSelWaves; ++i) cnt += whist[i][d];
-    }
-    const uint32_t excl = block_exclusive_scan(cnt, red, nullptr);
-    if (tid < 256 && cnt && excl < k && k <= excl + cnt) {
-      found[0] = d;
-      found[1] = excl;
-      found[2] = cnt;
+        for (int i = 0; i < kSelWaves; ++i) cnt += (whist[buf][i][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu;
+      }
+      incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane == 63) wtot[w] = incl;
     }
     __syncthreads();
-    prefix |= found[0] << shift;
+    if (tid < 256) {
+      uint32_t excl = incl - cnt;
+      for (int i = 0; i < w; ++i) excl += wtot[i];
+      if (cnt && excl < k && k <= excl + cnt) {
+        found[buf][0] = d;
+        found[buf][1] = excl;
+        found[buf][2] = cnt;
+      }
+    }
+    __syncthreads();
+    prefix |= found[buf][0] << shift;
     pmask |= dmask << shift;
-    k -= found[1];
-    const uint32_t bin = found[2];
-    __syncthreads();
+    k -= found[buf][1];
+    const uint32_t bin = found[buf][2];
     if (bin == k) break;  // the whole boundary bin is kept: no tie to break
     hb = shift - 1;
+    buf ^= 1;
   }
 
   // keep (u & pmask) > prefix, and the first k keys with (u & pmask) == prefix
