@@ -62,9 +62,13 @@ enum {
 
 /* Layer flags. */
 enum {
-  /* Not implemented in this version (returns STATEKV_ERR_UNSUPPORTED): one
-   * kept set per layer from scores summed over all query heads.  The default is
-   * per-KV-head selection (paperlayer App. A: sinks kept per layer and KV head). */
+  /* One kept set per layer: candidates are ranked by their importance summed
+   * over every query head of the layer, and every KV head keeps the same
+   * positions (rainbus method steps define the importance as a sum over
+   * queries without fixing whether heads share one kept set; this is the
+   * per-layer reading).  The state view's score rows stay per KV head.  The
+   * default is per-KV-head selection (paperlayer App. A: sinks kept per layer
+   * and KV head). */
   STATEKV_FLAG_SELECT_SHARED = 1u << 0,
   /* Wrap the detailed cache: token p goes to slot (p - position_offset) mod
    * detailed_capacity.  Without it, a frame that would overflow D fails with

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs 
     const int h = b / per_h;
     const int s0 = (b % per_h) * kRowsPerBlock;
     const int rows = min(kRowsPerBlock, g.newc - s0);
-    const int32_t* sel = g.sel + (int64_t)h * g.B + s0;
+    const int32_t* sel = g.sel + (int64_t)h * g.sel_stride + s0;
     if (tid < rows) {
       const int j = g.keep_all ? s0 + tid : sel[tid];
       g.pos_next[(int64_t)h * g.B + s0 + tid] =

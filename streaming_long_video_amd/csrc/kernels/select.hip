@@ -105,7 +105,6 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   const int tid = threadIdx.x, w = tid >> 6;
   const int pool = J.pool, budget = J.budget;
   const float* sp = J.sig_part + (int64_t)h * J.rt * J.ldsig;
-  int32_t* out = J.sel + (int64_t)h * J.ldsel;
 
   // importance = sum of the row tiles' partial column sums, in tile order;
   // every load of a batch (kLoad candidates x kRows row tiles per thread) is
@@ -144,6 +143,8 @@ __device__ void select_one_head(const SelectJob& J, int h) {
       }
     }
   }
+  if (!J.sel) return;  // scores only (per-head rows of the SHARED mode)
+  int32_t* out = J.sel + (int64_t)h * J.ldsel;
   if (pool <= budget) {
     for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
     return;
@@ -237,14 +238,23 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   }
 }
 
-// Blocks [0, n_select) select one KV head each; the remaining blocks sum the
-// split O partials (grid-stride over their share).
+// Blocks [0, n_select) handle one KV head each (scores, and the selection
+// unless J.sel is null); block n_select, when n_shared is 1, selects once for
+// the whole layer from the scores summed over every KV head (J2: the
+// Hkv x rt partial rows read as one list, h-major); the remaining blocks sum
+// the split O partials (grid-stride over their share).
 __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, int n_select,
+                                                                 SelectJob J2, int n_shared,
                                                                  SumJob Sj) {
   if ((int)blockIdx.x < n_select) {
     select_one_head(J, blockIdx.x);
     return;
   }
+  if ((int)blockIdx.x < n_select + n_shared) {
+    select_one_head(J2, 0);
+    return;
+  }
+  n_select += n_shared;
   const int64_t nb = gridDim.x - n_select;
   for (int64_t i = (int64_t)(blockIdx.x - n_select) * kSelThreads + threadIdx.x; i < Sj.n4;
        i += nb * kSelThreads) {
@@ -255,8 +265,8 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
 }
 
 namespace {
-hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj, int sum_blocks,
-                             const Stream& st) {
+hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& J2, int n_shared,
+                             const SumJob& Sj, int sum_blocks, const Stream& st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_sum_kernel),
@@ -266,17 +276,20 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SumJob& Sj,
     attr_set = true;
   }
   const size_t lds = (size_t)J.pool * sizeof(uint32_t);
-  hipExtLaunchKernelGGL(select_sum_kernel, dim3(n_select + sum_blocks), dim3(kSelThreads), lds, st.st, st.start, st.stop, 0,
-                     J, n_select, Sj);
+  hipExtLaunchKernelGGL(select_sum_kernel, dim3(n_select + n_shared + sum_blocks),
+                        dim3(kSelThreads), lds, st.st, st.start, st.stop, 0, J, n_select, J2,
+                        n_shared, Sj);
   return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
-                         const float* o_part, int S, int64_t o_elems, float* o,
+                         const float* o_part, int S, int64_t o_elems, float* o, bool shared,
                          const Stream& st) {
-  SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, sel, ldsel};
+  SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, shared ? nullptr : sel,
+                 ldsel};
+  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};
   int sum_blocks = 0;
@@ -284,7 +297,7 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
     const int64_t want = (Sj.n4 + kSelThreads - 1) / kSelThreads;
     sum_blocks = (int)(want < 1024 ? want : 1024);
   }
-  return launch_select_sum(J, hkv, Sj, sum_blocks, st);
+  return launch_select_sum(J, hkv, J2, shared ? 1 : 0, Sj, sum_blocks, st);
 }
 
 }  // namespace skv

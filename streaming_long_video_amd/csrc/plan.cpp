@@ -29,7 +29,6 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (Hq / Hkv > 16) return STATEKV_ERR_UNSUPPORTED;
   if (T > 4096) return STATEKV_ERR_UNSUPPORTED;
   if ((int64_t)B + T > kMaxPool) return STATEKV_ERR_UNSUPPORTED;
-  if (cfg->flags & STATEKV_FLAG_SELECT_SHARED) return STATEKV_ERR_UNSUPPORTED;
   if (cfg->detailed_capacity > ((int64_t)1 << 40)) return STATEKV_ERR_UNSUPPORTED;
   if (!(cfg->softmax_scale == cfg->softmax_scale) || isinf(cfg->softmax_scale))
     return STATEKV_ERR_INVALID_ARGUMENT;

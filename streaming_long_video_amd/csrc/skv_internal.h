@@ -48,7 +48,7 @@ hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
 // Standalone mode: rt = 1 and sig_part holds the scores.
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
                          int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
-                         const float* o_part, int S, int64_t o_elems, float* o,
+                         const float* o_part, int S, int64_t o_elems, float* o, bool shared,
                          const Stream& st);
 
 struct GatherArgs {
@@ -58,6 +58,7 @@ struct GatherArgs {
   const uint16_t* kf;       // [T][Hkv][D]
   const uint16_t* vf;
   const int32_t* sel;       // [Hkv][B] pool indices, ascending (ignored if keep_all)
+  int sel_stride;           // B, or 0 when one kept set serves every head (SHARED)
   uint16_t* kc_next;
   uint16_t* vc_next;
   int64_t* pos_next;

@@ -126,6 +126,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   if (L->mode == 2) return STATEKV_ERR_INVALID_ARGUMENT;
   const skv::Plan& p = L->plan;
   const bool ring = p.flags & STATEKV_FLAG_D_RING;
+  const bool shared = p.flags & STATEKV_FLAG_SELECT_SHARED;
   const int64_t next_len = (L->n + 1) * (int64_t)p.T;
   if (!ring && next_len > p.cap) return STATEKV_ERR_CAPACITY;
   if (L->n * (int64_t)p.T + p.T + p.offset > ((int64_t)1 << 62)) return STATEKV_ERR_CAPACITY;
@@ -158,7 +159,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
                                 p.B, a.S > 1 ? opart : nullptr, a.S,
-                                (int64_t)p.T * p.Hq * p.D, o, ks);
+                                (int64_t)p.T * p.Hq * p.D, o, shared, ks);
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
@@ -168,6 +169,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.kf = a.kf;
     g.vf = a.vf;
     g.sel = at<int32_t>(L, p.off_sel);
+    g.sel_stride = shared ? 0 : p.B;
     g.kc_next = at<uint16_t>(L, p.off_ck[nxt]);
     g.vc_next = at<uint16_t>(L, p.off_cv[nxt]);
     g.pos_next = at<int64_t>(L, p.off_cpos[nxt]);
@@ -369,7 +371,7 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
-                                       budget, nullptr, 1, 0, nullptr, st));
+                                       budget, nullptr, 1, 0, nullptr, false, st));
 }
 
 }  // extern "C"

@@ -92,7 +92,7 @@ int main() {
   c.flags = 1u << 7;
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
   c.flags = STATEKV_FLAG_SELECT_SHARED;
-  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK);
   c.flags = 0;
   c.num_splits = 3;
   CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 3 && p.stat_splits == 3);

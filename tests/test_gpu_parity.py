@@ -125,6 +125,35 @@ def test_1b_layer_free_running_and_teacher_forced():
     assert match >= SELECT_AGREEMENT * total
 
 
+def test_shared_selection_mode():
+    """SHARED: one kept set per layer from the importance summed over all query
+    heads; every KV head holds the same positions.  1B-like layer (Hkv = 2),
+    24 frames: teacher-forced against the oracle's shared mode, then free
+    running."""
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=24)
+    frames = framegen.stacked_frames(spec, workers=8)
+    qs, ks, vs = frames
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SELECT_SHARED)
+    layer, reports, _ = _run_teacher_forced(spec, layer=layer, orc_kw=dict(shared=True),
+                                            frames=frames)
+    _assert_reports(reports, exact_select=False)
+    snap = snapshot(layer)
+    np.testing.assert_array_equal(snap.pos[0], snap.pos[1])
+    check_caches_bitwise(layer, ks, vs)
+    layer2 = _layer(spec, flags=skv.STATEKV_FLAG_SELECT_SHARED)
+    orc = _oracle(spec, shared=True)
+    match = total = 0
+    for n in range(spec.n_frames):
+        layer2.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+        ref = orc.step(qs[n], ks[n], vs[n])
+        snap = snapshot(layer2)
+        kept = set(ref.kept_positions[0].tolist())
+        match += len(kept.intersection(snap.pos[0].tolist()))
+        total += len(kept)
+        np.testing.assert_array_equal(snap.pos[0], snap.pos[1])
+    assert match >= SELECT_AGREEMENT * total, (match, total)
+
+
 @pytest.mark.parametrize("shape", [
     # (Hq, Hkv, d, T, B, frames): ragged T, B not a tile multiple, G=1, G=16, T=1
     (6, 2, 128, 17, 50, 6),

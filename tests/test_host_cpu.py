@@ -53,11 +53,13 @@ def test_workspace_bytes_and_validation():
     assert n >= 2 * (2 * 4 * 4096 * 128 * 2 + 4 * 4096 * 8) + 2 * 4 * 131072 * 128 * 2
     for bad, status in [(dict(head_dim=96), -2), (dict(n_kv_heads=5), -1),
                         (dict(detailed_capacity=10), -1), (dict(state_budget=0), -1),
-                        (dict(flags=1), -2), (dict(flags=1 << 9), -1),
+                        (dict(flags=1 << 9), -1),
                         (dict(state_budget=32600), -2), (dict(frame_tokens=5000), -2)]:
         with pytest.raises(B.StateKVError) as e:
             B.statekv_workspace_bytes(_cfg(**bad))
         assert e.value.status == status, bad
+    # every defined flag is accepted (SELECT_SHARED, D_RING, NONCAUSAL_FRAME)
+    assert B.statekv_workspace_bytes(_cfg(flags=0b111)) >= n
 
 
 def test_init_views_and_argument_errors_are_host_side():
