@@ -291,3 +291,40 @@ def full_causal_attention(q_all, k_all, v_all, scale: Optional[float] = None,
         out[:, g, :] = (e / e.sum(axis=1, keepdims=True)) @ v[:, h, :]
     return out
 
+
+
+# ----------------------------------------------------------------------------
+# Decoding over the detailed state
+# ----------------------------------------------------------------------------
+
+def decode_attention(q, d_keys, d_values, scale: Optional[float] = None) -> np.ndarray:
+    """Attention of text-token queries over every token of the detailed state.
+
+    Once all frames are in, text generation is ordinary autoregressive decoding
+    conditioned on the detailed state D_N, which holds every original video
+    token (gist.science/nl, "Het Proces", decoding item; rainbus summary,
+    "核心方法" core method: standard text decoding over all video tokens after
+    the incremental cache build).  The text comes after the video, so every D
+    token is visible to every query; the queries' own text context (prompt and
+    generated tokens) is the standard decoder's cache and is not part of this
+    routine.
+
+    q: (M, Hq, d) queries; d_keys, d_values: (L, Hkv, d) the detailed state in
+    any token order (softmax attention does not depend on it).  Query head g
+    reads KV head floor(g / (Hq/Hkv)).  Returns (M, Hq, d) float64.
+    """
+    q = decode_bf16(q)
+    k = decode_bf16(d_keys)
+    v = decode_bf16(d_values)
+    M, Hq, d = q.shape
+    L, Hkv, _ = k.shape
+    G = Hq // Hkv
+    s = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((M, Hq, d))
+    for g in range(Hq):
+        h = g // G
+        z = s * (q[:, g, :] @ k[:, h, :].T)
+        z = z - z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        out[:, g, :] = (e / e.sum(axis=1, keepdims=True)) @ v[:, h, :]
+    return out

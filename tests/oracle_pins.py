@@ -194,6 +194,40 @@ def check_selection_and_caches() -> None:
             np.testing.assert_array_equal(dv, V)
 
 
+
+def check_decode_attention() -> None:
+    """Decoding over D: scalar Python loops with math.exp on a tiny case;
+    closed forms (one D token -> its value; all-zero keys -> mean of the KV
+    head's values); D token order does not matter; query head g reads KV head
+    g // G."""
+    rng = np.random.default_rng(7)
+    L, M, Hq, Hkv, d = 6, 2, 4, 2, 3
+    q = rng.standard_normal((M, Hq, d))
+    k = rng.standard_normal((L, Hkv, d))
+    v = rng.standard_normal((L, Hkv, d))
+    s = 0.7
+    out = so.decode_attention(q, k, v, scale=s)
+    G = Hq // Hkv
+    for m in range(M):
+        for g in range(Hq):
+            h = g // G
+            z = [s * sum(q[m, g, i] * k[j, h, i] for i in range(d)) for j in range(L)]
+            zmax = max(z)
+            w = [math.exp(x - zmax) for x in z]
+            tot = sum(w)
+            for i in range(d):
+                ref = sum(w[j] * v[j, h, i] for j in range(L)) / tot
+                assert abs(out[m, g, i] - ref) <= 1e-12, (m, g, i)
+    one = so.decode_attention(q, k[:1], v[:1])
+    for g in range(Hq):
+        assert np.allclose(one[:, g, :], v[0, g // G], rtol=0, atol=1e-15)
+    flat = so.decode_attention(q, np.zeros_like(k), v)
+    for g in range(Hq):
+        assert np.allclose(flat[:, g, :], v[:, g // G].mean(0), rtol=0, atol=1e-13)
+    perm = rng.permutation(L)
+    assert np.allclose(so.decode_attention(q, k[perm], v[perm]), so.decode_attention(q, k, v),
+                       rtol=0, atol=1e-13)
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -202,4 +236,5 @@ ALL_CHECKS = [
     check_probability_invariants,
     check_full_attention_equivalence,
     check_selection_and_caches,
+    check_decode_attention,
 ]

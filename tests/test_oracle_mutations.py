@@ -117,3 +117,39 @@ def test_gqa_mapping_mutant(monkeypatch):
     monkeypatch.setattr(so.StateKVOracle, "step", step)
     with pytest.raises(AssertionError):
         oracle_pins.check_gqa_head_mapping()
+
+
+_orig_decode = so.decode_attention
+
+
+def decode_drops_last_token(q, d_keys, d_values, scale=None):
+    return _orig_decode(q, np.asarray(d_keys)[:-1], np.asarray(d_values)[:-1], scale)
+
+
+def decode_heads_modulo(q, d_keys, d_values, scale=None):
+    q = np.asarray(q)
+    Hq, Hkv = q.shape[1], np.asarray(d_keys).shape[1]
+    G = Hq // Hkv
+    perm = np.array([(g % Hkv) * G + g // Hkv for g in range(Hq)])
+    return _orig_decode(q[:, perm, :], d_keys, d_values, scale)[:, np.argsort(perm), :]
+
+
+def decode_unscaled(q, d_keys, d_values, scale=None):
+    return _orig_decode(q, d_keys, d_values, 1.0)
+
+
+def decode_causal(q, d_keys, d_values, scale=None):
+    # as if query m stood at position m of the video
+    M = np.asarray(q).shape[0]
+    out = np.stack([_orig_decode(np.asarray(q)[m:m + 1], np.asarray(d_keys)[:m + 1],
+                                 np.asarray(d_values)[:m + 1], scale)[0] for m in range(M)])
+    return out
+
+
+@pytest.mark.parametrize("mutant", [decode_drops_last_token, decode_heads_modulo,
+                                     decode_unscaled, decode_causal],
+                         ids=lambda f: f.__name__)
+def test_decode_pin_catches_mutant(monkeypatch, mutant):
+    monkeypatch.setattr(so, "decode_attention", mutant)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_decode_attention()

@@ -10,7 +10,7 @@ from hypothesis import strategies as st
 
 import framegen
 import oracle_pins
-from oracle import StateKVOracle, full_causal_attention, select_top_b
+from oracle import StateKVOracle, decode_attention, full_causal_attention, select_top_b
 
 
 @pytest.mark.parametrize("check", oracle_pins.ALL_CHECKS, ids=lambda f: f.__name__)
@@ -35,6 +35,35 @@ def test_full_causal_attention_matches_torch_sdpa():
     # rows of the last queries only (the per-frame form used for baselines)
     tail = full_causal_attention(q[-9:], k, v, first_query=L - 9)
     np.testing.assert_allclose(tail, ours[-9:], rtol=0, atol=1e-13)
+
+
+def test_decode_attention_pins():
+    """Decoding over D: torch's float64 SDPA without a mask; the closed forms
+    of a single D token (output = its value) and of all-zero keys (uniform
+    weights: output = mean of the values of the query's KV head); and the
+    order of D's tokens does not matter."""
+    rng = np.random.default_rng(1)
+    L, M, Hq, Hkv, d = 53, 3, 6, 2, 16
+    q = rng.standard_normal((M, Hq, d))
+    k = rng.standard_normal((L, Hkv, d))
+    v = rng.standard_normal((L, Hkv, d))
+    ours = decode_attention(q, k, v)
+    G = Hq // Hkv
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    tv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    np.testing.assert_allclose(ours, ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-13)
+    one = decode_attention(q, k[:1], v[:1])
+    for g in range(Hq):
+        np.testing.assert_allclose(one[:, g, :], np.broadcast_to(v[0, g // G], (M, d)),
+                                   rtol=0, atol=1e-15)
+    flat = decode_attention(q, np.zeros_like(k), v)
+    for g in range(Hq):
+        np.testing.assert_allclose(flat[:, g, :], np.broadcast_to(v[:, g // G].mean(0), (M, d)),
+                                   rtol=0, atol=1e-13)
+    perm = rng.permutation(L)
+    np.testing.assert_allclose(decode_attention(q, k[perm], v[perm]), ours, rtol=0, atol=1e-13)
 
 
 def _brute_force_select(scores, positions, budget):
