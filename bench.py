@@ -22,6 +22,9 @@ Other measurements (not the headline line):
                        B in {1024, 2048, 4096}, N in {32, ..., 512}
     --mode depth28     28 independent 2B-shaped layers, layer-major per
                        frame, per-frame latency at frames 1, 9, 65, 256
+    --mode decode      decoding attention over the detailed state after the
+                       512-frame 8B stream (1 and 4 text tokens): time per
+                       call and HBM bandwidth of the decode kernel
 """
 
 from __future__ import annotations
@@ -340,6 +343,64 @@ def run_crossover(args):
 
 
 # ----------------------------------------------------------------------------
+# decoding over the detailed state after the whole 8B-like stream
+# ----------------------------------------------------------------------------
+
+def run_decode(args):
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload(args.workload)
+    T, Hq, Hkv, d, Bs, N = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
+                            spec.state_budget, spec.n_frames)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T)
+    chunk = 64
+    for n0 in range(0, N, chunk):
+        qs, ks, vs = framegen.stacked_frames(spec, n0, min(N, n0 + chunk),
+                                             workers=min(16, os.cpu_count() or 1))
+        up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        q_d, k_d, v_d = up(qs), up(ks), up(vs)
+        for i in range(q_d.shape[0]):
+            layer.prefill(q_d[i], k_d[i], v_d[i])
+    torch.cuda.synchronize()
+    out = {}
+    for M in args.decode_queries:
+        q = torch.from_numpy(framegen.text_queries(spec, M, 0).view(np.int16)).to(dev)
+        q = q.view(torch.bfloat16)
+        o = torch.empty((M, Hq, d), dtype=torch.float32, device=dev)
+        for _ in range(args.warmup):
+            layer.decode(q, out=o)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.decode(q, out=o)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        skv.statekv_profile_start(layer.handle, (1 << len(skv.STATEKV_KERNELS)) - 1,
+                                  64 * len(skv.STATEKV_KERNELS))
+        for _ in range(64):
+            layer.decode(q, out=o)
+        torch.cuda.synchronize()
+        prof = skv.statekv_profile_stop(layer.handle)
+        us = {k: ms / cnt * 1e3 for k, (ms, cnt) in prof.items() if cnt}
+        nbytes = 2.0 * Hkv * N * T * d * 2  # K and V of every D token
+        out[f"M={M}"] = {
+            "us_per_step": dt * 1e6, "decode_kernel_us": us.get("decode"),
+            "combine_us": us.get("split_sum"),
+            "d_bytes": nbytes,
+            "decode_kernel_gbs": nbytes / (us["decode"] * 1e-6) / 1e9 if us.get("decode") else None,
+            "frac_of_hbm_peak": (nbytes / (us["decode"] * 1e-6) / 1e9 / PEAK_HBM_GBS
+                                 if us.get("decode") else None),
+        }
+    print(json.dumps({"mode": "decode", "workload": args.workload, "frames": N,
+                      "tokens_per_kv_head": N * T, "results": out}), flush=True)
+
+
+# ----------------------------------------------------------------------------
 # 28 layers of the 2B shape, layer-major per frame
 # ----------------------------------------------------------------------------
 
@@ -385,7 +446,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=496)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--mode", choices=["headline", "crossover", "depth28"], default="headline")
+    ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode"],
+                    default="headline")
+    ap.add_argument("--decode-queries", type=int, nargs="+", default=[1, 4],
+                    help="text tokens per decoding call (decode mode)")
     ap.add_argument("--events", choices=["none", "dominant", "all"], default="none",
                     help="kernels timed with HIP events during the timed region (each timed "
                          "launch costs a few microseconds of dispatch serialisation)")
@@ -402,7 +466,8 @@ def main(argv=None):
         _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
-    {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28}[args.mode](args)
+    {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28,
+     "decode": run_decode}[args.mode](args)
 
 
 if __name__ == "__main__":

@@ -17,5 +17,6 @@ from .generator import (  # noqa: F401
     rope_rotate,
     sink_plan,
     stacked_frames,
+    text_queries,
     workload,
 )

@@ -208,6 +208,22 @@ def frame(spec: FrameSpec, n: int,
     return f64_to_bf16_bits(q), f64_to_bf16_bits(k), f64_to_bf16_bits(v)
 
 
+def text_queries(spec: FrameSpec, n_tokens: int, index: int = 0) -> np.ndarray:
+    """Queries of n_tokens text tokens that follow the video, as bf16 bits,
+    shape (n_tokens, Hq, d): N(0,1) values from ``default_rng([seed, -1,
+    index])``, RoPE at positions offset + N*T + i, plus the same query-side
+    sink component as the frames' queries."""
+    T, Hq, d = spec.frame_tokens, spec.n_q_heads, spec.head_dim
+    rng = np.random.default_rng([spec.seed, 2**31 - 1, index])
+    q = rng.standard_normal((n_tokens, Hq, d))
+    positions = spec.position_offset + spec.n_frames * T + np.arange(n_tokens, dtype=np.int64)
+    q = rope_rotate(q, positions, spec.rope_theta)
+    if spec.sinks:
+        u, _ = sink_plan(spec)
+        q = q + spec.query_sink * u
+    return f64_to_bf16_bits(q)
+
+
 def frames(spec: FrameSpec, start: int = 0, stop: Optional[int] = None
            ) -> Iterator[Tuple[np.ndarray, np.ndarray, np.ndarray]]:
     """Frames start..stop-1 (default: all) as bfloat16 bit patterns."""

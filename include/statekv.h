@@ -152,6 +152,26 @@ int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
 int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void* k,
                                  const void* v, float* o, void* stream);
 
+/* Decoding attention over the detailed state (the step after the video
+ * prefill): once the frames are in, text generation attends over D_N, which
+ * keeps every original video token (gist.science/nl, "Het Proces", decoding
+ * item; rainbus core method: ordinary text decoding over all video tokens).
+ * The text follows the video, so every live D token (slots [0, min(frames_seen
+ * * T, detailed_capacity)), any order) is visible to every query; the queries'
+ * own text context (prompt, generated tokens) is the caller's ordinary decoder
+ * cache and is not included.
+ *   q: device, [n_queries][Hq][d] bf16, 16-byte aligned, RoPE applied by the
+ *      caller at the text positions; query head g reads KV head g / G;
+ *   o: device, [n_queries][Hq][d] fp32, 16-byte aligned, written;
+ *   1 <= n_queries and G * n_queries <= 32 (else STATEKV_ERR_UNSUPPORTED);
+ *   frames_seen >= 1 (else STATEKV_ERR_INVALID_ARGUMENT).
+ * Works after statekv_prefill_frame or statekv_full_attention_frame and
+ * changes no layer state; uses the workspace's split-partial regions, so it
+ * must not overlap a prefill call of the same layer.  Kernels: DECODE (one
+ * wave per KV head and D split), then SPLIT_SUM (split combine). */
+int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_queries, float* o,
+                             void* stream);
+
 /* Views (host only). */
 int statekv_state(const statekv_layer* layer, statekv_state_view* out);
 int statekv_detailed_cache(const statekv_layer* layer, statekv_cache_view* out);
@@ -165,16 +185,17 @@ int statekv_free_layer(statekv_layer* layer);
 /* Human-readable name of a status code (static storage). */
 const char* statekv_status_string(int status);
 
-/* Kernels of statekv_prefill_frame, for the timing hooks below. */
+/* Kernels of the per-frame and decoding calls, for the timing hooks below. */
 enum {
   STATEKV_KERNEL_ATTN_STATS = 0, /* attention pass 1: row statistics           */
   STATEKV_KERNEL_ATTN_OUT = 1,   /* attention pass 2: O, importance partials   */
-  STATEKV_KERNEL_SPLIT_SUM = 2,  /* full attention only: split combine (the
-                                    StateKV path sums its split O partials in
-                                    the SELECT launch)                          */
+  STATEKV_KERNEL_SPLIT_SUM = 2,  /* split combine of the full-attention baseline
+                                    and of decoding (the StateKV path sums its
+                                    split O partials in the SELECT launch)      */
   STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select + O split sum */
   STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append         */
-  STATEKV_NUM_KERNELS = 5
+  STATEKV_KERNEL_DECODE = 5,     /* decoding over D: split partials            */
+  STATEKV_NUM_KERNELS = 6
 };
 
 /* Timing hooks for benchmarks (measurement only; results are unaffected).

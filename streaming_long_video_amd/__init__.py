@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     StateKVError,
     load_library,
     make_config,
+    statekv_decode_attention,
     statekv_detailed_cache,
     statekv_free_layer,
     statekv_full_attention_frame,

@@ -20,7 +20,7 @@ STATEKV_ERR_WORKSPACE = -3
 STATEKV_ERR_CAPACITY = -4
 STATEKV_ERR_HIP = -5
 
-STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather")
+STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather", "decode")
 
 STATEKV_FLAG_SELECT_SHARED = 1 << 0
 STATEKV_FLAG_D_RING = 1 << 1
@@ -86,7 +86,7 @@ def load_library() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing; build it with `python -m streaming_long_video_amd.build`")
+            f"{LIB_PATH} is missing; build it with `python streaming_long_video_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     cfgp = ctypes.POINTER(statekv_layer_config)
@@ -95,6 +95,7 @@ def load_library() -> ctypes.CDLL:
         "statekv_init_layer": (ctypes.c_int, [cfgp, P, ctypes.c_size_t, ctypes.POINTER(P)]),
         "statekv_prefill_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_full_attention_frame": (ctypes.c_int, [P, P, P, P, P, P]),
+        "statekv_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int32, P, P]),
         "statekv_state": (ctypes.c_int, [P, ctypes.POINTER(statekv_state_view)]),
         "statekv_detailed_cache": (ctypes.c_int, [P, ctypes.POINTER(statekv_cache_view)]),
         "statekv_reset_layer": (ctypes.c_int, [P]),
@@ -155,6 +156,11 @@ def statekv_full_attention_frame(layer: int, q: int, k: int, v: int, o: int,
                                  stream: int = 0) -> None:
     _check(load_library().statekv_full_attention_frame(layer, q, k, v, o, stream or None),
            "statekv_full_attention_frame")
+
+
+def statekv_decode_attention(layer: int, q: int, n_queries: int, o: int, stream: int = 0) -> None:
+    _check(load_library().statekv_decode_attention(layer, q, n_queries, o, stream or None),
+           "statekv_decode_attention")
 
 
 def statekv_state(layer: int) -> statekv_state_view:

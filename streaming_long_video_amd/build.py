@@ -1,6 +1,8 @@
 """Build libstatekv.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m streaming_long_video_amd.build [--verbose]
+    python streaming_long_video_amd/build.py [--verbose]
+
+(run as a file: importing the package loads the library, which this builds)
 
 Each source is compiled to an object in ``_build/`` next to this file, then
 linked into ``streaming_long_video_amd/libstatekv.so``.
@@ -28,6 +30,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "attention.hip"),
     os.path.join(CSRC, "kernels", "select.hip"),
     os.path.join(CSRC, "kernels", "gather.hip"),
+    os.path.join(CSRC, "kernels", "decode.hip"),
 ]
 
 ARCH = "gfx950"

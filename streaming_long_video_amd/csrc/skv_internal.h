@@ -79,6 +79,27 @@ hipError_t launch_append_only(const GatherArgs& g, int D, const Stream& st);
 // normalised O to o_out; otherwise unnormalised partials plus (m, l).
 hipError_t launch_full_attn(const AttnArgs& a, int D, const Stream& st);
 // Combines the unnormalised split partials of the full-attention baseline.
+// Decoding over the detailed state: one wave per (KV head, split); the four
+// waves of a workgroup write one merged partial ([parts][...] below).
+struct DecodeArgs {
+  const uint16_t* q;   // [M][Hq][D] bf16 text queries
+  const uint16_t* kd;  // [Hkv][cap][D] bf16 detailed keys
+  const uint16_t* vd;  // [Hkv][cap][D] bf16 detailed values
+  float* m_part;       // [parts][Hq][M] row max of raw logits per workgroup partial
+  float* l_part;       // [parts][Hq][M] row sum (relative to m)
+  float* o_part;       // [parts][M][Hq][D] unnormalised O
+  int64_t cap;         // D rows per KV head
+  int64_t len;         // live D rows per KV head (slots [0, len))
+  int M, Hq, Hkv, G, NS;
+  float scale_log2;
+};
+hipError_t launch_decode(const DecodeArgs& a, int D, const Stream& st);
+// Workgroup partials the decode launch writes per KV head for NS splits.
+int decode_parts(int ns);
+constexpr int kMaxDecodeParts = 1024;
+// o[M][Hq][D] from the workgroup partials, in a fixed order.
+hipError_t launch_decode_merge(const DecodeArgs& a, float* o, int D, const Stream& st);
+
 hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st);
 
 }  // namespace skv

@@ -242,6 +242,53 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   return STATEKV_OK;
 }
 
+int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries, float* o,
+                             void* stream) {
+  if (!L || !q || !o || n_queries < 1) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(o)) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  if (p.G * (int64_t)n_queries > 32) return STATEKV_ERR_UNSUPPORTED;
+  const int64_t hist = L->n * (int64_t)p.T;
+  const int64_t len = hist < p.cap ? hist : p.cap;
+  if (len <= 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  // splits (one wave each): about two waves per SIMD over all KV heads, at
+  // least 32 keys per wave; the workgroup partials (four splits each) must fit
+  // the split-partial regions of the workspace
+  const int64_t want = (2048 + p.Hkv - 1) / p.Hkv;
+  const int64_t by_len = (len + 31) / 32;
+  const int64_t opart = p.splits > p.full_splits ? p.splits : p.full_splits;
+  const int64_t parts_o = opart * p.T / n_queries;
+  const int64_t parts_ml = (int64_t)p.part_splits * p.tpad / n_queries;
+  int64_t max_parts = parts_o < parts_ml ? parts_o : parts_ml;
+  if (max_parts > skv::kMaxDecodeParts) max_parts = skv::kMaxDecodeParts;
+  int64_t ns = want < by_len ? want : by_len;
+  if (ns > 4 * max_parts) ns = 4 * max_parts;
+  if (ns < 1) ns = 1;
+  skv::DecodeArgs d = {};
+  d.q = static_cast<const uint16_t*>(q);
+  d.kd = at<uint16_t>(L, p.off_dk);
+  d.vd = at<uint16_t>(L, p.off_dv);
+  d.m_part = at<float>(L, p.off_m);
+  d.l_part = at<float>(L, p.off_l);
+  d.o_part = at<float>(L, p.off_o);
+  d.cap = p.cap;
+  d.len = len;
+  d.M = n_queries;
+  d.Hq = p.Hq;
+  d.Hkv = p.Hkv;
+  d.G = p.G;
+  d.NS = (int)ns;
+  d.scale_log2 = p.scale * kLog2e;
+  hipError_t e = timed(L, STATEKV_KERNEL_DECODE, st,
+                       [&](const skv::Stream& ks) { return skv::launch_decode(d, p.D, ks); });
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st,
+              [&](const skv::Stream& ks) { return skv::launch_decode_merge(d, o, p.D, ks); });
+  return hip_status(e);
+}
+
 int statekv_state(const statekv_layer* L, statekv_state_view* out) {
   if (!L || !out) return STATEKV_ERR_INVALID_ARGUMENT;
   const skv::Plan& p = L->plan;

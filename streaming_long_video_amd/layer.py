@@ -71,6 +71,23 @@ class Layer:
                                        out.data_ptr(), _stream_ptr(stream))
         return out
 
+    def decode(self, q, out=None, stream=None):
+        """Decoding attention of text queries q [M][Hq][d] (bf16) over every
+        token of the detailed cache; returns fp32 [M][Hq][d]."""
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or tuple(q.shape[1:]) != (self.Hq, self.d) \
+                or not q.is_contiguous() or q.device != self.workspace.device:
+            raise ValueError(f"q must be a contiguous bfloat16 tensor of shape (M, {self.Hq}, "
+                             f"{self.d}) on the layer's device")
+        M = q.shape[0]
+        if out is None:
+            out = torch.empty((M, self.Hq, self.d), dtype=torch.float32, device=q.device)
+        elif (out.dtype != torch.float32 or tuple(out.shape) != (M, self.Hq, self.d)
+              or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous float32 tensor of shape (M, Hq, d)")
+        B.statekv_decode_attention(self.handle, q.data_ptr(), M, out.data_ptr(),
+                                   _stream_ptr(stream))
+        return out
+
     # -- views -----------------------------------------------------------------
     def _ws_slice(self, ptr: int, nbytes: int, dtype, shape):
         off = ptr - self.workspace.data_ptr()

@@ -40,6 +40,7 @@ KERNELS = {
     "gather": r"gather_append_kernel<128>",
     "full_attn": r"attn_kernel<128, 3>",
     "full_combine": r"full_combine_kernel<128>",
+    "decode": r"decode_kernel<128>",
 }
 PROBE = r"neg"  # torch's negation kernel: the copy probe
 
@@ -47,6 +48,7 @@ SOURCES = (
     "csrc/kernels/attention.hip",
     "csrc/kernels/select.hip",
     "csrc/kernels/gather.hip",
+    "csrc/kernels/decode.hip",
 )
 
 

@@ -99,6 +99,20 @@ def test_ring_layout_rejects_full_attention_before_any_launch():
     B.statekv_free_layer(h)
 
 
+def test_decode_argument_errors_are_host_side():
+    cfg = _cfg()  # G = 7
+    nbytes = B.statekv_workspace_bytes(cfg)
+    fake = 1 << 40
+    h = B.statekv_init_layer(cfg, fake, nbytes)
+    for args, status in [((0, 1, fake), -1), ((fake, 0, fake), -1), ((fake + 2, 1, fake), -1),
+                         ((fake, 5, fake), -2),   # 7 * 5 > 32 rows
+                         ((fake, 1, fake), -1)]:  # no frame in D yet
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_decode_attention(h, *args)
+        assert e.value.status == status, args
+    B.statekv_free_layer(h)
+
+
 def test_select_argument_errors():
     with pytest.raises(B.StateKVError):
         B.statekv_select_topb(0, 10, 5, 0)
