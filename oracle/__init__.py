@@ -12,5 +12,7 @@ from .statekv_oracle import (  # noqa: F401
     frame_attention,
     full_causal_attention,
     importance_scores,
+    rope_at_positions,
+    round_to_bf16,
     select_top_b,
 )

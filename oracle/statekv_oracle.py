@@ -328,3 +328,42 @@ def decode_attention(q, d_keys, d_values, scale: Optional[float] = None) -> np.n
         e = np.exp(z)
         out[:, g, :] = (e / e.sum(axis=1, keepdims=True)) @ v[:, h, :]
     return out
+
+
+# ----------------------------------------------------------------------------
+# Rotary position embedding at the tokens' original positions
+# ----------------------------------------------------------------------------
+
+def rope_at_positions(x, positions, theta: float, scaling: float = 1.0) -> np.ndarray:
+    """Rotary position embedding of queries or keys at their original
+    positions, in float64.
+
+    The compressed state is physically shorter than the video but its tokens
+    keep the positions they arrived with, and the same RoPE scaling serves
+    cache building and text generation (paperlayer summary, section 3.3;
+    rainbus summary, prerequisites, "RoPE缩放": scaling stretches positions
+    past the trained length and must not change between the two phases).
+    Readings: the half-split pairing (component i pairs with i + d/2) at
+    frequency theta^(-2i/d); ``scaling`` divides the position (linear
+    interpolation; the pages give no value, 1 = none).
+
+    x: (T, H, d) values (bf16 bits or floats); positions: (T,).  Written as the
+    complex product (x_i + j x_{i+d/2}) * exp(j * angle).
+    """
+    x = decode_bf16(x)
+    d = x.shape[-1]
+    half = d // 2
+    freq = float(theta) ** (-2.0 * np.arange(half, dtype=np.float64) / d)
+    ang = (np.asarray(positions, dtype=np.float64)[:, None] / float(scaling)) * freq[None, :]
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * ang)[:, None, :]
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """float64 -> nearest bfloat16 (8 significant bits, ties to even), as
+    uint16 bit patterns.  Normal range only (finite values whose magnitude is
+    zero or at least 2^-126)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                    # x = m 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(m * 256.0), e - 8)  # np.rint: ties to even
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)

@@ -228,6 +228,41 @@ def check_decode_attention() -> None:
     assert np.allclose(so.decode_attention(q, k[perm], v[perm]), so.decode_attention(q, k, v),
                        rtol=0, atol=1e-13)
 
+
+def check_rope_and_rounding() -> None:
+    """RoPE: identity at position 0; a worked example (d = 4, theta = 100:
+    the second pair turns by 0.1 rad per position); pair norms preserved;
+    q.k after rotation depends only on the position difference; linear
+    scaling divides the position.  bf16 rounding: hand-picked ties and
+    near-ties."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 2, 8))
+    assert np.allclose(so.rope_at_positions(x, np.zeros(3), 1e4), x, rtol=0, atol=0)
+    e1 = np.zeros((1, 1, 4))
+    e1[0, 0, 1] = 1.0
+    r = so.rope_at_positions(e1, np.array([2]), 100.0)[0, 0]
+    assert np.allclose(r, [0.0, math.cos(0.2), 0.0, math.sin(0.2)], rtol=0, atol=1e-15)
+    pos = np.array([5, 1000, 123456])
+    y = so.rope_at_positions(x, pos, 1e6)
+    half = 4
+    assert np.allclose(x[..., :half] ** 2 + x[..., half:] ** 2,
+                       y[..., :half] ** 2 + y[..., half:] ** 2, rtol=1e-12, atol=0)
+    q = rng.standard_normal((1, 1, 8))
+    k = rng.standard_normal((1, 1, 8))
+    dots = []
+    for p0 in (0, 17, 4096):
+        qr = so.rope_at_positions(q, np.array([p0 + 9]), 1e4)
+        kr = so.rope_at_positions(k, np.array([p0]), 1e4)
+        dots.append(float(np.sum(qr * kr)))
+    assert max(dots) - min(dots) <= 1e-10, dots
+    assert np.allclose(so.rope_at_positions(x, pos, 1e6, scaling=4.0),
+                       so.rope_at_positions(x, pos / 4.0, 1e6), rtol=0, atol=1e-12)
+    vals = np.array([1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 3 * 2.0 ** -8,
+                     -2.5, 3.0 * 2.0 ** -100, 0.0])
+    want = np.array([1.0, 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -6, -2.5, 3.0 * 2.0 ** -100, 0.0])
+    got = (so.round_to_bf16(vals).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, want), got
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -237,4 +272,5 @@ ALL_CHECKS = [
     check_full_attention_equivalence,
     check_selection_and_caches,
     check_decode_attention,
+    check_rope_and_rounding,
 ]

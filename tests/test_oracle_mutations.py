@@ -153,3 +153,50 @@ def test_decode_pin_catches_mutant(monkeypatch, mutant):
     monkeypatch.setattr(so, "decode_attention", mutant)
     with pytest.raises(AssertionError):
         oracle_pins.check_decode_attention()
+
+
+_orig_rope = so.rope_at_positions
+_orig_round = so.round_to_bf16
+
+
+def rope_adjacent_pairs(x, positions, theta, scaling=1.0):
+    # pairs (2i, 2i+1) instead of (i, i + d/2)
+    x = so.decode_bf16(x)
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    return _orig_rope(x[..., perm], positions, theta, scaling)[..., inv]
+
+
+def rope_wrong_frequency(x, positions, theta, scaling=1.0):
+    return _orig_rope(x, positions, theta ** 2, scaling)
+
+
+def rope_sign_flipped(x, positions, theta, scaling=1.0):
+    return _orig_rope(x, -np.asarray(positions, dtype=np.float64), theta, scaling)
+
+
+def rope_scaling_multiplies(x, positions, theta, scaling=1.0):
+    return _orig_rope(x, np.asarray(positions, dtype=np.float64) * scaling, theta, 1.0)
+
+
+def round_truncates(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def round_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.sign(m) * np.floor(np.abs(m) * 256.0 + 0.5), e - 8)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("rope_at_positions", rope_adjacent_pairs), ("rope_at_positions", rope_wrong_frequency),
+    ("rope_at_positions", rope_sign_flipped), ("rope_at_positions", rope_scaling_multiplies),
+    ("round_to_bf16", round_truncates), ("round_to_bf16", round_ties_away)],
+    ids=lambda v: v if isinstance(v, str) else v.__name__)
+def test_rope_pin_catches_mutant(monkeypatch, name, mutant):
+    monkeypatch.setattr(so, name, mutant)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_rope_and_rounding()
