@@ -115,6 +115,9 @@ class FrameSpec:
     query_sink: float = 0.5
     n_layers: int = 1
     layer_seed_base: Optional[int] = None  # seed of layer l = layer_seed_base + l
+    # False: queries and keys are left unrotated (for a consumer that applies
+    # the rotary embedding itself); the draws are the same either way
+    rotated: bool = True
 
     @property
     def group(self) -> int:
@@ -190,8 +193,9 @@ def frame_f64(spec: FrameSpec, n: int,
     k = rng.standard_normal((T, Hkv, d))
     v = rng.standard_normal((T, Hkv, d))
     positions = spec.position_offset + n * T + np.arange(T, dtype=np.int64)
-    q = rope_rotate(q, positions, spec.rope_theta)
-    k = rope_rotate(k, positions, spec.rope_theta)
+    if spec.rotated:
+        q = rope_rotate(q, positions, spec.rope_theta)
+        k = rope_rotate(k, positions, spec.rope_theta)
     if spec.sinks:
         u, spos = plan if plan is not None else sink_plan(spec)
         q = q + spec.query_sink * u
@@ -217,7 +221,8 @@ def text_queries(spec: FrameSpec, n_tokens: int, index: int = 0) -> np.ndarray:
     rng = np.random.default_rng([spec.seed, 2**31 - 1, index])
     q = rng.standard_normal((n_tokens, Hq, d))
     positions = spec.position_offset + spec.n_frames * T + np.arange(n_tokens, dtype=np.int64)
-    q = rope_rotate(q, positions, spec.rope_theta)
+    if spec.rotated:
+        q = rope_rotate(q, positions, spec.rope_theta)
     if spec.sinks:
         u, _ = sink_plan(spec)
         q = q + spec.query_sink * u

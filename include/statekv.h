@@ -91,6 +91,19 @@ typedef struct statekv_layer_config {
   int64_t position_offset;   /* original position of frame 0, token 0            */
   float softmax_scale;       /* logit scale; <= 0 means 1/sqrt(d)                */
   uint32_t flags;            /* STATEKV_FLAG_*                                   */
+  /* Rotary embedding inside the library.  rope_theta > 0: q and k arrive
+   * unrotated and every per-frame call rotates them at the frame's original
+   * positions p = position_offset + n*T + t before anything else (C and D then
+   * hold rotated keys; paperlayer section 3.3: positions stay virtual although
+   * C is physically shorter); statekv_rope rotates other tokens (text queries)
+   * with the same parameters.  Pairing (x_i, x_{i+d/2}), angle
+   * (p / rope_scaling) * rope_theta^(-2i/d), angles and their cosine and sine
+   * in double precision, the rotation in fp32, the result rounded to bf16
+   * (nearest, ties to even).  rope_theta = 0: q and k arrive rotated.
+   * rope_scaling: linear position interpolation, <= 0 means 1 (the pages
+   * require one value for cache building and generation but give none). */
+  float rope_theta;
+  float rope_scaling;
 } statekv_layer_config;
 
 /* View of the compressed state C_n (borrowed; valid until the next
@@ -172,6 +185,15 @@ int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void
 int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_queries, float* o,
                              void* stream);
 
+/* Rotate n_tokens x n_heads rows of d bf16 values in place (device,
+ * [n_tokens][n_heads][d], 16-byte aligned) at positions first_position + i,
+ * with the layer's rope_theta and rope_scaling (text queries before
+ * statekv_decode_attention, so that cache building and generation share one
+ * RoPE configuration).  STATEKV_ERR_INVALID_ARGUMENT if the layer has
+ * rope_theta = 0 or an argument is out of range. */
+int statekv_rope(statekv_layer* layer, void* x, int32_t n_tokens, int32_t n_heads,
+                 int64_t first_position, void* stream);
+
 /* Views (host only). */
 int statekv_state(const statekv_layer* layer, statekv_state_view* out);
 int statekv_detailed_cache(const statekv_layer* layer, statekv_cache_view* out);
@@ -195,7 +217,8 @@ enum {
   STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select + O split sum */
   STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append         */
   STATEKV_KERNEL_DECODE = 5,     /* decoding over D: split partials            */
-  STATEKV_NUM_KERNELS = 6
+  STATEKV_KERNEL_ROPE = 6,       /* in-library rotary embedding of the frame   */
+  STATEKV_NUM_KERNELS = 7
 };
 
 /* Timing hooks for benchmarks (measurement only; results are unaffected).

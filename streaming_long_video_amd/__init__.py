@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     statekv_profile_start,
     statekv_profile_stop,
     statekv_reset_layer,
+    statekv_rope,
     statekv_select_topb,
     statekv_state,
     statekv_status_string,

@@ -20,7 +20,8 @@ STATEKV_ERR_WORKSPACE = -3
 STATEKV_ERR_CAPACITY = -4
 STATEKV_ERR_HIP = -5
 
-STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather", "decode")
+STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather", "decode",
+                   "rope")
 
 STATEKV_FLAG_SELECT_SHARED = 1 << 0
 STATEKV_FLAG_D_RING = 1 << 1
@@ -45,6 +46,8 @@ class statekv_layer_config(ctypes.Structure):
         ("position_offset", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+        ("rope_theta", ctypes.c_float),
+        ("rope_scaling", ctypes.c_float),
     ]
 
 
@@ -96,6 +99,7 @@ def load_library() -> ctypes.CDLL:
         "statekv_prefill_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_full_attention_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int32, P, P]),
+        "statekv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]),
         "statekv_state": (ctypes.c_int, [P, ctypes.POINTER(statekv_state_view)]),
         "statekv_detailed_cache": (ctypes.c_int, [P, ctypes.POINTER(statekv_cache_view)]),
         "statekv_reset_layer": (ctypes.c_int, [P]),
@@ -121,11 +125,12 @@ def _check(status: int, what: str) -> None:
 
 def make_config(n_q_heads, n_kv_heads, head_dim, frame_tokens, state_budget,
                 detailed_capacity, position_offset=0, softmax_scale=0.0, flags=0,
-                num_splits=0) -> statekv_layer_config:
+                num_splits=0, rope_theta=0.0, rope_scaling=0.0) -> statekv_layer_config:
     return statekv_layer_config(int(n_q_heads), int(n_kv_heads), int(head_dim),
                                 int(frame_tokens), int(state_budget), int(num_splits),
                                 int(detailed_capacity), int(position_offset),
-                                float(softmax_scale), int(flags))
+                                float(softmax_scale), int(flags), float(rope_theta),
+                                float(rope_scaling))
 
 
 def statekv_status_string(status: int) -> str:
@@ -161,6 +166,12 @@ def statekv_full_attention_frame(layer: int, q: int, k: int, v: int, o: int,
 def statekv_decode_attention(layer: int, q: int, n_queries: int, o: int, stream: int = 0) -> None:
     _check(load_library().statekv_decode_attention(layer, q, n_queries, o, stream or None),
            "statekv_decode_attention")
+
+
+def statekv_rope(layer: int, x: int, n_tokens: int, n_heads: int, first_position: int,
+                 stream: int = 0) -> None:
+    _check(load_library().statekv_rope(layer, x, n_tokens, n_heads, first_position,
+                                       stream or None), "statekv_rope")
 
 
 def statekv_state(layer: int) -> statekv_state_view:

@@ -31,6 +31,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "select.hip"),
     os.path.join(CSRC, "kernels", "gather.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
+    os.path.join(CSRC, "kernels", "rope.hip"),
 ]
 
 ARCH = "gfx950"

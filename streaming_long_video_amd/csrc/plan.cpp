@@ -32,6 +32,10 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (cfg->detailed_capacity > ((int64_t)1 << 40)) return STATEKV_ERR_UNSUPPORTED;
   if (!(cfg->softmax_scale == cfg->softmax_scale) || isinf(cfg->softmax_scale))
     return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!(cfg->rope_theta >= 0.f) || isinf(cfg->rope_theta) || cfg->rope_theta == 1.f)
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!(cfg->rope_scaling == cfg->rope_scaling) || isinf(cfg->rope_scaling))
+    return STATEKV_ERR_INVALID_ARGUMENT;
 
   Plan q = {};
   q.Hq = Hq;
@@ -44,6 +48,8 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   q.offset = cfg->position_offset;
   q.scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : (float)(1.0 / sqrt((double)D));
   q.flags = cfg->flags;
+  q.rope_theta = cfg->rope_theta;
+  q.rope_scaling = cfg->rope_scaling > 0.f ? cfg->rope_scaling : 1.0;
   q.ntblk = ceil_div(T, kTokBlk);
   q.nqblk = q.G * q.ntblk;
   q.rt = ceil_div(q.nqblk, kRowBlk);
@@ -92,6 +98,9 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   q.off_sig = off; off = align_up(off + (size_t)Hkv * q.rt * q.ldsig * 4, A);
   q.off_scores = off; off = align_up(off + (size_t)Hkv * q.ldsig * 4, A);
   q.off_sel = off; off = align_up(off + (size_t)Hkv * B * 4, A);
+  const bool rope = q.rope_theta > 0.0;
+  q.off_qrot = off; off = align_up(off + (rope ? (size_t)T * Hq * D * 2 : 0), A);
+  q.off_krot = off; off = align_up(off + (rope ? (size_t)T * Hkv * D * 2 : 0), A);
   q.total = off;
   *p = q;
   return STATEKV_OK;

@@ -23,6 +23,8 @@ struct Plan {
   int32_t Hq, Hkv, G, D, T, B;
   int64_t cap, offset;
   float scale;        // softmax scale applied to the logits
+  double rope_theta;  // > 0: the library rotates q and k (else they arrive rotated)
+  double rope_scaling;
   uint32_t flags;
   // attention grid
   int32_t ntblk;      // ceil(T / kTokBlk): token blocks per query head
@@ -41,6 +43,7 @@ struct Plan {
   size_t off_dk, off_dv;
   size_t off_m, off_l, off_o;
   size_t off_sig, off_scores, off_sel;
+  size_t off_qrot, off_krot;  // rotated frame q / k (only with rope_theta > 0)
   size_t total;
 };
 

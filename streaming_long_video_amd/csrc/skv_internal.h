@@ -100,6 +100,20 @@ constexpr int kMaxDecodeParts = 1024;
 // o[M][Hq][D] from the workgroup partials, in a fixed order.
 hipError_t launch_decode_merge(const DecodeArgs& a, float* o, int D, const Stream& st);
 
+// Rotary embedding of n_tokens x n_rows rows of D bf16 values (x -> y; y may
+// be x) at positions first_position + token; optionally a second tensor of
+// the same tokens with n_rows2 rows (x2 -> y2) in the same launch.
+struct RopeArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const uint16_t* x2;
+  uint16_t* y2;
+  int n_tokens, n_rows, n_rows2;
+  int64_t first_position;
+  double theta, scaling;
+};
+hipError_t launch_rope(const RopeArgs& r, int D, const Stream& st);
+
 hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st);
 
 }  // namespace skv

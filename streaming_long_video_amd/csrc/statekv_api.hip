@@ -82,6 +82,28 @@ hipError_t timed(statekv_layer* L, int kernel, hipStream_t st, F&& launch) {
   return launch(skv::Stream(st));
 }
 
+// With in-library RoPE: rotate the frame's q and k into the workspace at the
+// frame's original positions and hand back the rotated copies.
+hipError_t rotate_frame(statekv_layer* L, hipStream_t st, const void** q, const void** k) {
+  const skv::Plan& p = L->plan;
+  if (!(p.rope_theta > 0.0)) return hipSuccess;
+  skv::RopeArgs r = {};
+  r.x = static_cast<const uint16_t*>(*q);
+  r.y = at<uint16_t>(L, p.off_qrot);
+  r.x2 = static_cast<const uint16_t*>(*k);
+  r.y2 = at<uint16_t>(L, p.off_krot);
+  r.n_tokens = p.T;
+  r.n_rows = p.Hq;
+  r.n_rows2 = p.Hkv;
+  r.first_position = p.offset + L->n * (int64_t)p.T;
+  r.theta = p.rope_theta;
+  r.scaling = p.rope_scaling;
+  *q = r.y;
+  *k = r.y2;
+  return timed(L, STATEKV_KERNEL_ROPE, st,
+               [&](const skv::Stream& ks) { return skv::launch_rope(r, p.D, ks); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,6 +160,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   const int pool = c + p.T;
   const int newc = pool < p.B ? pool : p.B;
 
+  hipError_t e = rotate_frame(L, st, &q, &k);
   skv::AttnArgs a = attn_args(L, q, k, v);
   a.kc = at<uint16_t>(L, p.off_ck[cur]);
   a.vc = at<uint16_t>(L, p.off_cv[cur]);
@@ -150,8 +173,9 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   a.Sst = skv::stat_splits_for_pool(p, pool);
   skv::AttnArgs a1 = a;
   a1.S = a.Sst;
-  hipError_t e = timed(L, STATEKV_KERNEL_ATTN_STATS, st,
-                       [&](const skv::Stream& ks) { return skv::launch_attn_stats(a1, p.D, ks); });
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_ATTN_STATS, st,
+              [&](const skv::Stream& ks) { return skv::launch_attn_stats(a1, p.D, ks); });
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&](const skv::Stream& ks) { return skv::launch_attn_out(a, p.D, ks); });
   if (e == hipSuccess)
@@ -209,6 +233,7 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   hipStream_t st = static_cast<hipStream_t>(stream);
   L->mode = 2;
 
+  hipError_t e = rotate_frame(L, st, &q, &k);
   skv::GatherArgs g = {};
   g.kf = static_cast<const uint16_t*>(k);
   g.vf = static_cast<const uint16_t*>(v);
@@ -220,8 +245,9 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   g.B = p.B;
   g.T = p.T;
   g.Hkv = p.Hkv;
-  hipError_t e =
-      timed(L, STATEKV_KERNEL_GATHER, st, [&](const skv::Stream& ks) { return skv::launch_append_only(g, p.D, ks); });
+  if (e == hipSuccess)
+    e = timed(L, STATEKV_KERNEL_GATHER, st,
+              [&](const skv::Stream& ks) { return skv::launch_append_only(g, p.D, ks); });
 
   skv::AttnArgs a = attn_args(L, q, k, v);
   a.kc = at<uint16_t>(L, p.off_dk);
@@ -287,6 +313,27 @@ int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries,
     e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st,
               [&](const skv::Stream& ks) { return skv::launch_decode_merge(d, o, p.D, ks); });
   return hip_status(e);
+}
+
+int statekv_rope(statekv_layer* L, void* x, int32_t n_tokens, int32_t n_heads,
+                 int64_t first_position, void* stream) {
+  if (!L || !x || n_tokens < 1 || n_heads < 1 || first_position < 0)
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x)) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  if (!(p.rope_theta > 0.0)) return STATEKV_ERR_INVALID_ARGUMENT;
+  skv::RopeArgs r = {};
+  r.x = static_cast<const uint16_t*>(x);
+  r.y = static_cast<uint16_t*>(x);
+  r.n_tokens = n_tokens;
+  r.n_rows = n_heads;
+  r.first_position = first_position;
+  r.theta = p.rope_theta;
+  r.scaling = p.rope_scaling;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(L, STATEKV_KERNEL_ROPE, st, [&](const skv::Stream& ks) {
+    return skv::launch_rope(r, p.D, ks);
+  }));
 }
 
 int statekv_state(const statekv_layer* L, statekv_state_view* out) {

@@ -28,10 +28,11 @@ class Layer:
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, frame_tokens: int,
                  state_budget: int, detailed_capacity: int, position_offset: int = 0,
                  softmax_scale: float = 0.0, flags: int = 0, num_splits: int = 0,
+                 rope_theta: float = 0.0, rope_scaling: float = 0.0,
                  device: Optional[torch.device] = None):
         self.cfg = B.make_config(n_q_heads, n_kv_heads, head_dim, frame_tokens, state_budget,
                                  detailed_capacity, position_offset, softmax_scale, flags,
-                                 num_splits)
+                                 num_splits, rope_theta, rope_scaling)
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
         self.T, self.B = frame_tokens, state_budget
         self.capacity = detailed_capacity
@@ -70,6 +71,17 @@ class Layer:
         B.statekv_full_attention_frame(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                        out.data_ptr(), _stream_ptr(stream))
         return out
+
+    def rope(self, x, first_position: int, stream=None):
+        """Rotate x [n][heads][d] (bf16, in place) at positions first_position + i
+        with the layer's RoPE parameters; returns x."""
+        if x.dtype != torch.bfloat16 or x.dim() != 3 or x.shape[2] != self.d \
+                or not x.is_contiguous() or x.device != self.workspace.device:
+            raise ValueError("x must be a contiguous bfloat16 (n, heads, d) tensor on the "
+                             "layer's device")
+        B.statekv_rope(self.handle, x.data_ptr(), x.shape[0], x.shape[1], int(first_position),
+                       _stream_ptr(stream))
+        return x
 
     def decode(self, q, out=None, stream=None):
         """Decoding attention of text queries q [M][Hq][d] (bf16) over every

@@ -49,6 +49,7 @@ SOURCES = (
     "csrc/kernels/select.hip",
     "csrc/kernels/gather.hip",
     "csrc/kernels/decode.hip",
+    "csrc/kernels/rope.hip",
 )
 
 

@@ -43,7 +43,9 @@ static void check_layout(const statekv_layer_config& c) {
       {p.off_o, (size_t)std::max(p.splits, p.full_splits) * p.T * p.Hq * p.D * 4},
       {p.off_sig, (size_t)p.Hkv * p.rt * p.ldsig * 4},
       {p.off_scores, (size_t)p.Hkv * p.ldsig * 4},
-      {p.off_sel, (size_t)p.Hkv * p.B * 4}};
+      {p.off_sel, (size_t)p.Hkv * p.B * 4},
+      {p.off_qrot, p.rope_theta > 0 ? (size_t)p.T * p.Hq * p.D * 2 : 0},
+      {p.off_krot, p.rope_theta > 0 ? (size_t)p.T * p.Hkv * p.D * 2 : 0}};
   std::sort(r.begin(), r.end());
   for (size_t i = 0; i < r.size(); ++i) {
     CHECK(r[i].first % 256 == 0);
@@ -73,6 +75,19 @@ int main() {
   check_layout(cfg(2, 1, 64, 16, 32, 128));
   check_layout(cfg(6, 2, 128, 17, 50, 102));
   check_layout(cfg(16, 1, 64, 4096, 28672, 4096));
+  {
+    statekv_layer_config r = cfg(28, 4, 128, 256, 4096, 131072);
+    r.rope_theta = 1e6f;
+    check_layout(r);
+    skv::Plan p;
+    CHECK(skv::make_plan(&r, &p) == STATEKV_OK && p.rope_theta == 1e6 && p.rope_scaling == 1.0);
+    r.rope_scaling = 4.f;
+    CHECK(skv::make_plan(&r, &p) == STATEKV_OK && p.rope_scaling == 4.0);
+    r.rope_theta = 1.f;  // every frequency would be 1
+    CHECK(skv::make_plan(&r, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+    r.rope_theta = -5.f;
+    CHECK(skv::make_plan(&r, &p) == STATEKV_ERR_INVALID_ARGUMENT);
+  }
   skv::Plan p;
   statekv_layer_config c = cfg(28, 4, 128, 256, 4096, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.stat_splits == 18 && p.rt == 7);

@@ -113,6 +113,31 @@ def test_decode_argument_errors_are_host_side():
     B.statekv_free_layer(h)
 
 
+def test_rope_configuration_and_argument_errors():
+    for bad in (dict(rope_theta=-1.0), dict(rope_theta=1.0), dict(rope_theta=float("inf")),
+                dict(rope_scaling=float("nan"))):
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_workspace_bytes(_cfg(**bad))
+        assert e.value.status == -1, bad
+    plain = B.statekv_workspace_bytes(_cfg())
+    # the rotated frame copies: T*Hq*d + T*Hkv*d bf16
+    assert B.statekv_workspace_bytes(_cfg(rope_theta=1e6)) >= plain + 256 * 32 * 128 * 2
+    fake = 1 << 40
+    h = B.statekv_init_layer(_cfg(), fake, plain)
+    with pytest.raises(B.StateKVError) as e:  # the layer has no RoPE configuration
+        B.statekv_rope(h, fake, 1, 1, 0)
+    assert e.value.status == -1
+    B.statekv_free_layer(h)
+    cfg = _cfg(rope_theta=1e6)
+    h = B.statekv_init_layer(cfg, fake, B.statekv_workspace_bytes(cfg))
+    for args in ((0, 1, 1, 0), (fake + 2, 1, 1, 0), (fake, 0, 1, 0), (fake, 1, 0, 0),
+                 (fake, 1, 1, -1)):
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_rope(h, *args)
+        assert e.value.status == -1, args
+    B.statekv_free_layer(h)
+
+
 def test_select_argument_errors():
     with pytest.raises(B.StateKVError):
         B.statekv_select_topb(0, 10, 5, 0)
