@@ -32,15 +32,48 @@ __device__ inline uint32_t score_key(float x) {
   return u > 0x7F800000u ? 0u : u;  // NaN, -0 and negatives rank lowest
 }
 
+// Wave-level primitives on DPP (every lane of the wave active).
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele within each 16-lane
+// row (row_shr 1, 2, 4, 8, zero fill), then row 0 / 2 totals into rows 1 / 3
+// (row_bcast:15) and the rows-0-1 total into rows 2-3 (row_bcast:31).
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
+}
+__device__ inline uint32_t wave_inclusive_sum(uint32_t v) {
+  v += dpp_u32<0x111, 0xF>(v);
+  v += dpp_u32<0x112, 0xF>(v);
+  v += dpp_u32<0x114, 0xF>(v);
+  v += dpp_u32<0x118, 0xF>(v);
+  v += dpp_u32<0x142, 0xA>(v);
+  v += dpp_u32<0x143, 0xC>(v);
+  return v;
+}
+// Minimum and maximum over the 64 lanes (result read from lane 63); lanes
+// without a DPP source keep their own value.
+template <int CTRL, int ROWS>
+__device__ inline uint32_t dpp_keep(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+__device__ inline void wave_min_max(uint32_t& mn, uint32_t& mx) {
+#define SKV_STEP(C, R)            \
+  mn = min(mn, dpp_keep<C, R>(mn)); \
+  mx = max(mx, dpp_keep<C, R>(mx));
+  SKV_STEP(0x111, 0xF)
+  SKV_STEP(0x112, 0xF)
+  SKV_STEP(0x114, 0xF)
+  SKV_STEP(0x118, 0xF)
+  SKV_STEP(0x142, 0xA)
+  SKV_STEP(0x143, 0xC)
+#undef SKV_STEP
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+}
+
 // Exclusive prefix sum over the workgroup; also returns the total.
 __device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint32_t v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  const uint32_t v = wave_inclusive_sum(x);
   if (lane == 63) sh[w] = v;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -56,11 +89,7 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32
 }
 
 __device__ inline uint32_t block_min_max(uint32_t mn, uint32_t mx, uint32_t* sh, uint32_t* out_max) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-  }
+  wave_min_max(mn, mx);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sh[w] = mn;
@@ -186,12 +215,7 @@ __device__ void select_one_head(const SelectJob& J, int h) {
 #pragma unroll
         for (int i = 0; i < kSelWaves; ++i) cnt += (whist[buf][i][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu;
       }
-      incl = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
+      incl = wave_inclusive_sum(cnt);
       if (lane == 63) wtot[w] = incl;
     }
     __syncthreads();
