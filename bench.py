@@ -175,7 +175,9 @@ def run_headline(args):
         return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
 
     q_all, k_all, v_all = up(qs), up(ks), up(vs)
-    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T, num_splits=args.splits)
+    flags = skv.STATEKV_FLAG_C_IN_D if args.state_layout == "positions" else 0
+    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T, num_splits=args.splits,
+                      flags=flags)
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
     for n in range(W):
         layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
@@ -233,7 +235,8 @@ def run_headline(args):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, RoPE at original positions, "
                 "10 planted temporal-sink keys in frames 0-3)",
-        "config": {"workload": args.workload, "n_q_heads": Hq, "n_kv_heads": Hkv,
+        "config": {"workload": args.workload, "state_layout": args.state_layout,
+                   "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": d, "frame_tokens": T, "state_budget": Bs,
                    "frames": N, "detailed_capacity": N * T},
     }
@@ -459,6 +462,8 @@ def main(argv=None):
                     help="run a plain device copy of this size before the timed region "
                          "(reference kernel for rocprofv3 byte counters)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = auto)")
+    ap.add_argument("--state-layout", choices=["rows", "positions"], default="rows",
+                    help="C as its own K/V rows (copied on update) or as positions into D")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)

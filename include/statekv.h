@@ -75,7 +75,12 @@ enum {
    * STATEKV_ERR_CAPACITY. */
   STATEKV_FLAG_D_RING = 1u << 1,
   /* Frame tokens see every frame token, not only earlier ones. */
-  STATEKV_FLAG_NONCAUSAL_FRAME = 1u << 2
+  STATEKV_FLAG_NONCAUSAL_FRAME = 1u << 2,
+  /* Keep C as the positions of its tokens only: attention reads their K and V
+   * rows from D (every token is there), and the state update moves positions
+   * instead of K/V rows.  Needs a linear D (with D_RING:
+   * STATEKV_ERR_UNSUPPORTED).  The state view's k and v are then NULL. */
+  STATEKV_FLAG_C_IN_D = 1u << 3
 };
 
 typedef struct statekv_layer statekv_layer; /* opaque, host memory */

@@ -7,6 +7,7 @@ build script.  Importing it loads the library and fails if it is missing.
 """
 
 from ._binding import (  # noqa: F401
+    STATEKV_FLAG_C_IN_D,
     STATEKV_FLAG_D_RING,
     STATEKV_FLAG_NONCAUSAL_FRAME,
     STATEKV_FLAG_SELECT_SHARED,

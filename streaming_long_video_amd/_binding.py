@@ -26,6 +26,7 @@ STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather", "d
 STATEKV_FLAG_SELECT_SHARED = 1 << 0
 STATEKV_FLAG_D_RING = 1 << 1
 STATEKV_FLAG_NONCAUSAL_FRAME = 1 << 2
+STATEKV_FLAG_C_IN_D = 1 << 3
 
 
 class StateKVError(RuntimeError):

@@ -124,15 +124,22 @@ __device__ inline uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Row of the state buffer that holds state token j of KV head h: j itself, or
+// (with the state kept as positions into D) the D row of its position.
+__device__ inline int64_t state_row(const AttnArgs& a, int h, int j) {
+  return a.cpos ? a.cpos[(int64_t)h * a.ldcp + j] - a.cpos_base : (int64_t)j;
+}
+
 // One 16-byte chunk (8 bf16) of pool row j, columns [col, col+8); zero past the pool.
 template <int D>
-__device__ inline u32x4 pool_chunk(const uint16_t* state, const uint16_t* frame, int64_t ldc,
-                                   int Hkv, int h, int c, int pool, int j, int col) {
+__device__ inline u32x4 pool_chunk(const AttnArgs& a, const uint16_t* state,
+                                   const uint16_t* frame, int h, int pool, int j, int col) {
   u32x4 v = {0u, 0u, 0u, 0u};
-  if (j < c)
-    v = *reinterpret_cast<const u32x4*>(state + ((int64_t)h * ldc + j) * D + col);
+  if (j < a.c)
+    v = *reinterpret_cast<const u32x4*>(state + ((int64_t)h * a.ldc + state_row(a, h, j)) * D +
+                                        col);
   else if (j < pool)
-    v = *reinterpret_cast<const u32x4*>(frame + ((int64_t)(j - c) * Hkv + h) * D + col);
+    v = *reinterpret_cast<const u32x4*>(frame + ((int64_t)(j - a.c) * a.Hkv + h) * D + col);
   return v;
 }
 
@@ -153,8 +160,7 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * kThreads;
-      k[i] = pool_chunk<D>(a.kc, a.kf, a.ldc, a.Hkv, h, a.c, pool, key0 + ch / (D / 8),
-                           (ch % (D / 8)) * 8);
+      k[i] = pool_chunk<D>(a, a.kc, a.kf, h, pool, key0 + ch / (D / 8), (ch % (D / 8)) * 8);
     }
     if constexpr (WITH_V) {
 #pragma unroll
@@ -162,8 +168,8 @@ struct TileStage {
         const int it = tid + i * kThreads;
         if (VPART && it >= VITEMS) continue;
         const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
-        v0[i] = pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, a.c, pool, key0 + 2 * kp, dc);
-        v1[i] = pool_chunk<D>(a.vc, a.vf, a.ldc, a.Hkv, h, a.c, pool, key0 + 2 * kp + 1, dc);
+        v0[i] = pool_chunk<D>(a, a.vc, a.vf, h, pool, key0 + 2 * kp, dc);
+        v1[i] = pool_chunk<D>(a, a.vc, a.vf, h, pool, key0 + 2 * kp + 1, dc);
       }
     }
   }
@@ -185,6 +191,29 @@ struct TileStage {
         const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
         v0[i] = *reinterpret_cast<const u32x4*>(vb + (2 * kp) * D + dc);
         v1[i] = *reinterpret_cast<const u32x4*>(vb + (2 * kp + 1) * D + dc);
+      }
+    }
+  }
+
+  // State tile kept as positions into D: the rows come from the D rows in
+  // `rows` (looked up one tile ahead, see StateRows).
+  template <class Rows>
+  __device__ inline void load_state_rows(const AttnArgs& a, int h, const Rows& rows, int tid) {
+    const uint16_t* kb = a.kc + (int64_t)h * a.ldc * D;
+    const uint16_t* vb = a.vc + (int64_t)h * a.ldc * D;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ch = tid + i * kThreads;
+      k[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)rows.k[i] * D + (ch % (D / 8)) * 8);
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VIT; ++i) {
+        const int it = tid + i * kThreads;
+        if (VPART && it >= VITEMS) continue;
+        const int dc = (it / (kKeyTile / 2)) * 8;
+        v0[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)rows.v0[i] * D + dc);
+        v1[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)rows.v1[i] * D + dc);
       }
     }
   }
@@ -214,8 +243,37 @@ struct TileStage {
   }
 };
 
-template <int D, int PASS>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+// D rows of the state tokens one thread stages for a state tile (same
+// row assignment as TileStage), when the state is kept as positions into D.
+template <int D, bool WITH_V>
+struct StateRows {
+  using TS = TileStage<D, WITH_V>;
+  int32_t k[TS::KCH];
+  int32_t v0[WITH_V ? TS::VIT : 1], v1[WITH_V ? TS::VIT : 1];
+
+  __device__ inline void load(const AttnArgs& a, int h, int key0, int tid) {
+#pragma unroll
+    for (int i = 0; i < TS::KCH; ++i)
+      k[i] = (int32_t)state_row(a, h, key0 + (tid + i * kThreads) / (D / 8));
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < TS::VIT; ++i) {
+        const int it = tid + i * kThreads;
+        if (TS::VPART && it >= TS::VITEMS) continue;
+        const int kp = it % (kKeyTile / 2);
+        v0[i] = (int32_t)state_row(a, h, key0 + 2 * kp);
+        v1[i] = (int32_t)state_row(a, h, key0 + 2 * kp + 1);
+      }
+    }
+  }
+};
+
+// Second launch bound = minimum waves per SIMD: the statistics pass runs two
+// workgroups per CU (four waves per SIMD, at most 128 registers), the other
+// passes one (two waves per SIMD).
+// CIND: the state is kept as positions into D (a.cpos set).
+template <int D, int PASS, bool CIND>
+__global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnArgs a) {
   constexpr int QB = kQBlkPerWave;
   constexpr int KT = kKeyTile;
   constexpr int NKK = D / 16;  // k-steps of the QK^T MFMA
@@ -268,10 +326,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // the first key tile's global loads go out first, so that their latency
   // overlaps the Q and row-statistics loads below
   TileStage<D, WITH_V> stage;
+  // With the state kept as positions into D, the D rows of the next state
+  // tile are looked up one tile before its K/V loads go out.
+  StateRows<D, WITH_V> rows;
   auto stage_load = [&](int key0) __attribute__((always_inline)) {
-    if (key0 + KT <= c) stage.load_state(a, h, key0, tid);
-    else stage.load(a, h, pool, key0, tid);
+    if (key0 + KT <= c) {
+      if constexpr (CIND) {
+        stage.load_state_rows(a, h, rows, tid);
+        if (key0 + 2 * KT <= c) rows.load(a, h, key0 + KT, tid);
+      } else {
+        stage.load_state(a, h, key0, tid);
+      }
+    } else {
+      stage.load(a, h, pool, key0, tid);
+    }
   };
+  if (CIND && (tile_lo + 1) * KT <= c) rows.load(a, h, tile_lo * KT, tid);
   if (tile_end > tile_lo) stage_load(tile_lo * KT);
 
   bf16x8 qreg[QB][NKK];
@@ -658,13 +728,24 @@ __global__ __launch_bounds__(256) void full_combine_kernel(AttnArgs a, float* o)
 namespace {
 int attn_grid(const AttnArgs& a) { return a.Hkv * a.S * a.rt; }
 
+template <int PASS, bool CIND>
+hipError_t launch_pass_as(const AttnArgs& a, int D, const Stream& st) {
+  if (D == 128)
+    hipExtLaunchKernelGGL((attn_kernel<128, PASS, CIND>), dim3(attn_grid(a)), dim3(kThreads), 0,
+                          st.st, st.start, st.stop, 0, a);
+  else
+    hipExtLaunchKernelGGL((attn_kernel<64, PASS, CIND>), dim3(attn_grid(a)), dim3(kThreads), 0,
+                          st.st, st.start, st.stop, 0, a);
+  return hipGetLastError();
+}
+
 template <int PASS>
 hipError_t launch_pass(const AttnArgs& a, int D, const Stream& st) {
-  if (D == 128)
-    hipExtLaunchKernelGGL((attn_kernel<128, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st.st, st.start, st.stop, 0, a);
-  else
-    hipExtLaunchKernelGGL((attn_kernel<64, PASS>), dim3(attn_grid(a)), dim3(kThreads), 0, st.st, st.start, st.stop, 0, a);
-  return hipGetLastError();
+  if constexpr (PASS == 3) {
+    return launch_pass_as<3, false>(a, D, st);  // the baseline's state is D itself
+  } else {
+    return a.cpos ? launch_pass_as<PASS, true>(a, D, st) : launch_pass_as<PASS, false>(a, D, st);
+  }
 }
 }  // namespace
 

@@ -1,6 +1,7 @@
 // State update and detailed-cache append.
 //
-//   gather: C_n[h][s] = pool[h][sel[h][s]] for s < |C_n|, where the pool is
+//   gather: C_n[h][s] = pool[h][sel[h][s]] for s < |C_n| (the positions only,
+//     when the state is kept as positions into D), where the pool is
 //     [C_{n-1}[h] ; frame tokens of KV head h] -- key row, value row and the
 //     original position (paper.rainbus.top, method-steps section: the top-B
 //     candidates of previous state plus frame become the new compressed state;
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs 
       g.pos_next[(int64_t)h * g.B + s0 + tid] =
           j < g.c ? g.pos_prev[(int64_t)h * g.B + j] : g.pos_offset + g.frame_base + (j - g.c);
     }
+    if (!g.kc_next) return;  // the state is kept as positions into D: no row copy
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int it = tid + i * kCopyThreads;

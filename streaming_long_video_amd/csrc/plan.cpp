@@ -23,8 +23,10 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (cfg->position_offset < 0) return STATEKV_ERR_INVALID_ARGUMENT;
   if (cfg->num_splits < 0) return STATEKV_ERR_INVALID_ARGUMENT;
   if (cfg->flags & ~(uint32_t)(STATEKV_FLAG_SELECT_SHARED | STATEKV_FLAG_D_RING |
-                               STATEKV_FLAG_NONCAUSAL_FRAME))
+                               STATEKV_FLAG_NONCAUSAL_FRAME | STATEKV_FLAG_C_IN_D))
     return STATEKV_ERR_INVALID_ARGUMENT;
+  if ((cfg->flags & STATEKV_FLAG_C_IN_D) && (cfg->flags & STATEKV_FLAG_D_RING))
+    return STATEKV_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return STATEKV_ERR_UNSUPPORTED;
   if (Hq / Hkv > 16) return STATEKV_ERR_UNSUPPORTED;
   if (T > 4096) return STATEKV_ERR_UNSUPPORTED;
@@ -83,9 +85,10 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   size_t off = 0;
   const size_t c_rows = (size_t)Hkv * B;
   const size_t d_rows = (size_t)Hkv * (size_t)q.cap;
+  const size_t c_kv = (cfg->flags & STATEKV_FLAG_C_IN_D) ? 0 : c_rows * D * 2;
   for (int i = 0; i < 2; ++i) {
-    q.off_ck[i] = off; off = align_up(off + c_rows * D * 2, A);
-    q.off_cv[i] = off; off = align_up(off + c_rows * D * 2, A);
+    q.off_ck[i] = off; off = align_up(off + c_kv, A);
+    q.off_cv[i] = off; off = align_up(off + c_kv, A);
     q.off_cpos[i] = off; off = align_up(off + c_rows * 8, A);
   }
   q.off_dk = off; off = align_up(off + d_rows * D * 2, A);

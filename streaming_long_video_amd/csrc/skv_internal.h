@@ -30,6 +30,10 @@ struct AttnArgs {
   float* o_out;        // [T][Hq][D] fp32 when S == 1, else [S][T][Hq][D] partials
   float* sig_part;     // [Hkv][rt][ldsig] per-row-tile score partials
   int64_t ldc;         // state rows per KV head (B)
+  const int64_t* cpos;  // null, or [Hkv][ldcp] positions of the state tokens: state token
+                        // j of head h is then row cpos[h*ldcp + j] - cpos_base of kc/vc
+  int64_t cpos_base;
+  int ldcp;
   int T, Hq, Hkv, G;
   int c;               // live state rows; pool = c + T
   int ntblk, nqblk, rt, tpad;
@@ -59,7 +63,7 @@ struct GatherArgs {
   const uint16_t* vf;
   const int32_t* sel;       // [Hkv][B] pool indices, ascending (ignored if keep_all)
   int sel_stride;           // B, or 0 when one kept set serves every head (SHARED)
-  uint16_t* kc_next;
+  uint16_t* kc_next;        // null: positions only (state kept as positions into D)
   uint16_t* vc_next;
   int64_t* pos_next;
   uint16_t* kd;             // [Hkv][cap][D] detailed cache (null: no append)

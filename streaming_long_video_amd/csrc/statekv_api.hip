@@ -149,6 +149,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   const skv::Plan& p = L->plan;
   const bool ring = p.flags & STATEKV_FLAG_D_RING;
   const bool shared = p.flags & STATEKV_FLAG_SELECT_SHARED;
+  const bool c_in_d = p.flags & STATEKV_FLAG_C_IN_D;
   const int64_t next_len = (L->n + 1) * (int64_t)p.T;
   if (!ring && next_len > p.cap) return STATEKV_ERR_CAPACITY;
   if (L->n * (int64_t)p.T + p.T + p.offset > ((int64_t)1 << 62)) return STATEKV_ERR_CAPACITY;
@@ -162,9 +163,18 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
 
   hipError_t e = rotate_frame(L, st, &q, &k);
   skv::AttnArgs a = attn_args(L, q, k, v);
-  a.kc = at<uint16_t>(L, p.off_ck[cur]);
-  a.vc = at<uint16_t>(L, p.off_cv[cur]);
-  a.ldc = p.B;
+  if (c_in_d) {  // state rows are D rows, found through the state's positions
+    a.kc = at<uint16_t>(L, p.off_dk);
+    a.vc = at<uint16_t>(L, p.off_dv);
+    a.ldc = p.cap;
+    a.cpos = at<int64_t>(L, p.off_cpos[cur]);
+    a.cpos_base = p.offset;
+    a.ldcp = p.B;
+  } else {
+    a.kc = at<uint16_t>(L, p.off_ck[cur]);
+    a.vc = at<uint16_t>(L, p.off_cv[cur]);
+    a.ldc = p.B;
+  }
   a.c = c;
   a.S = skv::splits_for_pool(p, pool);
   float* opart = at<float>(L, p.off_o);
@@ -187,15 +197,15 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
-    g.kc_prev = a.kc;
-    g.vc_prev = a.vc;
+    g.kc_prev = c_in_d ? nullptr : a.kc;
+    g.vc_prev = c_in_d ? nullptr : a.vc;
     g.pos_prev = at<int64_t>(L, p.off_cpos[cur]);
     g.kf = a.kf;
     g.vf = a.vf;
     g.sel = at<int32_t>(L, p.off_sel);
     g.sel_stride = shared ? 0 : p.B;
-    g.kc_next = at<uint16_t>(L, p.off_ck[nxt]);
-    g.vc_next = at<uint16_t>(L, p.off_cv[nxt]);
+    g.kc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_ck[nxt]);
+    g.vc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_cv[nxt]);
     g.pos_next = at<int64_t>(L, p.off_cpos[nxt]);
     g.kd = at<uint16_t>(L, p.off_dk);
     g.vd = at<uint16_t>(L, p.off_dv);
@@ -209,7 +219,8 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.newc = newc;
     g.keep_all = pool <= p.B;
     g.ring = ring;
-    e = timed(L, STATEKV_KERNEL_GATHER, st, [&](const skv::Stream& ks) { return skv::launch_gather_append(g, p.D, ks); });
+    e = timed(L, STATEKV_KERNEL_GATHER, st,
+              [&](const skv::Stream& ks) { return skv::launch_gather_append(g, p.D, ks); });
   }
   if (e != hipSuccess) return hip_status(e);
   L->cur = nxt;
@@ -241,7 +252,6 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   g.vd = at<uint16_t>(L, p.off_dv);
   g.cap = p.cap;
   g.frame_base = hist;
-  g.pos_offset = p.offset;
   g.B = p.B;
   g.T = p.T;
   g.Hkv = p.Hkv;
@@ -340,8 +350,9 @@ int statekv_state(const statekv_layer* L, statekv_state_view* out) {
   if (!L || !out) return STATEKV_ERR_INVALID_ARGUMENT;
   const skv::Plan& p = L->plan;
   statekv_state_view v = {};
-  v.k = at<uint16_t>(L, p.off_ck[L->cur]);
-  v.v = at<uint16_t>(L, p.off_cv[L->cur]);
+  const bool c_in_d = p.flags & STATEKV_FLAG_C_IN_D;
+  v.k = c_in_d ? nullptr : at<uint16_t>(L, p.off_ck[L->cur]);
+  v.v = c_in_d ? nullptr : at<uint16_t>(L, p.off_cv[L->cur]);
   v.pos = at<int64_t>(L, p.off_cpos[L->cur]);
   v.last_scores = at<float>(L, p.off_scores);
   v.count = L->c;

@@ -36,6 +36,8 @@ class Layer:
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
         self.T, self.B = frame_tokens, state_budget
         self.capacity = detailed_capacity
+        self.position_offset = position_offset
+        self.flags = flags
         nbytes = B.statekv_workspace_bytes(self.cfg)
         dev = torch.device("cuda") if device is None else torch.device(device)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -107,13 +109,14 @@ class Layer:
         return self.workspace[off:off + nbytes].view(dtype).view(shape)
 
     def state(self):
-        """C_n as workspace views: dict(k, v, pos, count, scores, pool, frames_seen)."""
+        """C_n as workspace views: dict(k, v, pos, count, scores, pool, frames_seen);
+        k and v are None when the layer keeps C as positions into D."""
         v = B.statekv_state(self.handle)
         Hkv, Bc, d = v.n_kv_heads, v.capacity, v.head_dim
         rows = Hkv * Bc * d * 2
         return {
-            "k": self._ws_slice(v.k, rows, torch.bfloat16, (Hkv, Bc, d)),
-            "v": self._ws_slice(v.v, rows, torch.bfloat16, (Hkv, Bc, d)),
+            "k": self._ws_slice(v.k, rows, torch.bfloat16, (Hkv, Bc, d)) if v.k else None,
+            "v": self._ws_slice(v.v, rows, torch.bfloat16, (Hkv, Bc, d)) if v.v else None,
             "pos": self._ws_slice(v.pos, Hkv * Bc * 8, torch.int64, (Hkv, Bc)),
             "scores": self._ws_slice(v.last_scores, Hkv * v.scores_stride * 4, torch.float32,
                                      (Hkv, v.scores_stride)),

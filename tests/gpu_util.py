@@ -49,8 +49,15 @@ def snapshot(layer) -> StateSnapshot:
     st = layer.state()
     c, pool = st["count"], st["pool"]
     pos = st["pos"][:, :c].cpu().numpy()
-    k = to_bits(st["k"][:, :c])
-    v = to_bits(st["v"][:, :c])
+    if st["k"] is None:  # C kept as positions into D: read its rows from D
+        dc = layer.detailed_cache()
+        dk, dv = to_bits(dc["k"]), to_bits(dc["v"])
+        base = layer.position_offset
+        k = np.stack([dk[h][pos[h] - base] for h in range(pos.shape[0])])
+        v = np.stack([dv[h][pos[h] - base] for h in range(pos.shape[0])])
+    else:
+        k = to_bits(st["k"][:, :c])
+        v = to_bits(st["v"][:, :c])
     sc = st["scores"][:, :pool].cpu().numpy()
     H = pos.shape[0]
     return StateSnapshot(c, [pos[h] for h in range(H)], [k[h] for h in range(H)],
@@ -110,9 +117,12 @@ def check_caches_bitwise(layer, frames_k, frames_v, n_frames: Optional[int] = No
     np.testing.assert_array_equal(dk, np.transpose(K, (1, 0, 2)))
     np.testing.assert_array_equal(dv, np.transpose(V, (1, 0, 2)))
     pos = st["pos"][:, :c].cpu().numpy()
+    for h in range(pos.shape[0]):
+        assert np.all(np.diff(pos[h]) > 0)
+    if st["k"] is None:  # C kept as positions into D: nothing else to compare
+        return
     ck = to_bits(st["k"][:, :c])
     cv = to_bits(st["v"][:, :c])
     for h in range(pos.shape[0]):
-        assert np.all(np.diff(pos[h]) > 0)
         np.testing.assert_array_equal(ck[h], dk[h][pos[h]])
         np.testing.assert_array_equal(cv[h], dv[h][pos[h]])

@@ -125,6 +125,33 @@ def test_1b_layer_free_running_and_teacher_forced():
     assert match >= SELECT_AGREEMENT * total
 
 
+@pytest.mark.parametrize("flags", ["c_in_d", "c_in_d_shared"])
+def test_state_kept_as_positions_into_d(flags):
+    """C_IN_D: the state holds positions only and attention reads its rows
+    from D.  1B-like layer, 24 frames: teacher-forced against the oracle (the
+    state's rows read back from D), then bit-identical outputs to the default
+    layout on the same stream."""
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=24)
+    frames = framegen.stacked_frames(spec, workers=8)
+    qs, ks, vs = frames
+    f = skv.STATEKV_FLAG_C_IN_D
+    shared = flags.endswith("shared")
+    if shared:
+        f |= skv.STATEKV_FLAG_SELECT_SHARED
+    layer, reports, _ = _run_teacher_forced(spec, layer=_layer(spec, flags=f),
+                                            orc_kw=dict(shared=shared), frames=frames)
+    _assert_reports(reports, exact_select=False)
+    assert layer.state()["k"] is None
+    check_caches_bitwise(layer, ks, vs)
+    a = _layer(spec, flags=f)
+    b = _layer(spec, flags=f & ~skv.STATEKV_FLAG_C_IN_D)
+    for n in range(spec.n_frames):
+        oa = a.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        ob = b.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        np.testing.assert_array_equal(oa, ob)
+        np.testing.assert_array_equal(snapshot(a).pos[0], snapshot(b).pos[0])
+
+
 def test_shared_selection_mode():
     """SHARED: one kept set per layer from the importance summed over all query
     heads; every KV head holds the same positions.  1B-like layer (Hkv = 2),

@@ -60,6 +60,11 @@ def test_workspace_bytes_and_validation():
         assert e.value.status == status, bad
     # every defined flag is accepted (SELECT_SHARED, D_RING, NONCAUSAL_FRAME)
     assert B.statekv_workspace_bytes(_cfg(flags=0b111)) >= n
+    # C kept as positions into D: no K/V copies of C, and it needs a linear D
+    assert B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_C_IN_D)) <= n - 4 * 4096 * 128 * 2 * 2
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_C_IN_D | B.STATEKV_FLAG_D_RING))
+    assert e.value.status == -2
 
 
 def test_init_views_and_argument_errors_are_host_side():
