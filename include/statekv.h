@@ -80,7 +80,12 @@ enum {
    * rows from D (every token is there), and the state update moves positions
    * instead of K/V rows.  Needs a linear D (with D_RING:
    * STATEKV_ERR_UNSUPPORTED).  The state view's k and v are then NULL. */
-  STATEKV_FLAG_C_IN_D = 1u << 3
+  STATEKV_FLAG_C_IN_D = 1u << 3,
+  /* Recency window instead of importance: keep the B most recent candidates
+   * (the rule StateKV is compared against -- rainbus core method: ReKV keeps
+   * the last R frames; paperlayer App. A.3 measures the gap).  Importance
+   * scores are still computed and reported. */
+  STATEKV_FLAG_SELECT_RECENT = 1u << 4
 };
 
 typedef struct statekv_layer statekv_layer; /* opaque, host memory */
@@ -205,6 +210,18 @@ int statekv_detailed_cache(const statekv_layer* layer, statekv_cache_view* out);
 
 /* Forget every frame (host only): empty C and D, frames_seen = 0. */
 int statekv_reset_layer(statekv_layer* layer);
+
+/* Resume a layer from a checkpoint (host only).  The natural checkpoint of a
+ * layer after frame n-1 is (C_n rows with their positions, D[0 : n*T), n):
+ * the caller writes them into the regions that statekv_state and
+ * statekv_detailed_cache report (C rows [0, count) of k, v and pos in
+ * ascending position; D as the detailed view lays it out), then calls this
+ * so that the next statekv_prefill_frame processes frame frames_seen.
+ * count must equal min(B, frames_seen * T) (STATEKV_ERR_INVALID_ARGUMENT
+ * otherwise), and a linear D must hold frames_seen * T tokens
+ * (STATEKV_ERR_CAPACITY).  The last frame's scores are not part of the
+ * checkpoint (last_pool becomes 0). */
+int statekv_restore_layer(statekv_layer* layer, int64_t frames_seen, int32_t count);
 
 /* Release the host handle (the workspace stays the caller's). */
 int statekv_free_layer(statekv_layer* layer);

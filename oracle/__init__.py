@@ -14,5 +14,6 @@ from .statekv_oracle import (  # noqa: F401
     importance_scores,
     rope_at_positions,
     round_to_bf16,
+    select_most_recent,
     select_top_b,
 )

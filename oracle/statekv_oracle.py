@@ -122,6 +122,17 @@ def select_top_b(scores: np.ndarray, positions: np.ndarray, budget: int) -> np.n
 # Streaming layer
 # ----------------------------------------------------------------------------
 
+def select_most_recent(positions: np.ndarray, budget: int) -> np.ndarray:
+    """The recency rule StateKV is compared against: keep the ``budget``
+    candidates with the largest original positions (a window over the most
+    recent tokens; rainbus summary, core method: ReKV keeps the last R frames,
+    StateKV selects by importance instead; paperlayer App. A.3 measures the gap
+    between the two).  Returns pool indices in ascending position order."""
+    positions = np.asarray(positions)
+    keep = np.argsort(positions, kind="stable")[::-1][: min(budget, len(positions))]
+    return np.sort(keep)
+
+
 @dataclasses.dataclass
 class FrameResult:
     o: np.ndarray                    # (T, Hq, d) float64 attention output
@@ -144,7 +155,8 @@ class StateKVOracle:
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  frame_tokens: int, state_budget: int, scale: Optional[float] = None,
                  causal: bool = True, shared: bool = False, position_offset: int = 0,
-                 detailed_capacity: Optional[int] = None, ring: bool = False):
+                 detailed_capacity: Optional[int] = None, ring: bool = False,
+                 recency: bool = False):
         if n_q_heads % n_kv_heads:
             raise ValueError("n_q_heads must be a multiple of n_kv_heads")
         self.Hq, self.Hkv, self.d = n_q_heads, n_kv_heads, head_dim
@@ -155,6 +167,7 @@ class StateKVOracle:
         self.offset = position_offset
         self.capacity = detailed_capacity
         self.ring = ring
+        self.recency = recency  # keep the most recent B candidates instead
         self.n = 0
         self.c_pos = [np.zeros(0, dtype=np.int64) for _ in range(n_kv_heads)]
         self.c_k: List[Optional[np.ndarray]] = [None] * n_kv_heads
@@ -247,7 +260,12 @@ class StateKVOracle:
             keep_shared = select_top_b(total, pools[0], self.B)
         kept = []
         for h in range(Hkv):
-            keep = keep_shared if self.shared else select_top_b(scores[h], pools[h], self.B)
+            if self.recency:
+                keep = select_most_recent(pools[h], self.B)
+            elif self.shared:
+                keep = keep_shared
+            else:
+                keep = select_top_b(scores[h], pools[h], self.B)
             self.c_pos[h] = pools[h][keep]
             self.c_k[h] = raw_k[h][keep]
             self.c_v[h] = raw_v[h][keep]

@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     STATEKV_FLAG_C_IN_D,
     STATEKV_FLAG_D_RING,
     STATEKV_FLAG_NONCAUSAL_FRAME,
+    STATEKV_FLAG_SELECT_RECENT,
     STATEKV_FLAG_SELECT_SHARED,
     STATEKV_KERNELS,
     StateKVError,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     statekv_profile_start,
     statekv_profile_stop,
     statekv_reset_layer,
+    statekv_restore_layer,
     statekv_rope,
     statekv_select_topb,
     statekv_state,

@@ -27,6 +27,7 @@ STATEKV_FLAG_SELECT_SHARED = 1 << 0
 STATEKV_FLAG_D_RING = 1 << 1
 STATEKV_FLAG_NONCAUSAL_FRAME = 1 << 2
 STATEKV_FLAG_C_IN_D = 1 << 3
+STATEKV_FLAG_SELECT_RECENT = 1 << 4
 
 
 class StateKVError(RuntimeError):
@@ -104,6 +105,7 @@ def load_library() -> ctypes.CDLL:
         "statekv_state": (ctypes.c_int, [P, ctypes.POINTER(statekv_state_view)]),
         "statekv_detailed_cache": (ctypes.c_int, [P, ctypes.POINTER(statekv_cache_view)]),
         "statekv_reset_layer": (ctypes.c_int, [P]),
+        "statekv_restore_layer": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32]),
         "statekv_free_layer": (ctypes.c_int, [P]),
         "statekv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "statekv_select_topb": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P]),
@@ -190,6 +192,11 @@ def statekv_detailed_cache(layer: int) -> statekv_cache_view:
 
 def statekv_reset_layer(layer: int) -> None:
     _check(load_library().statekv_reset_layer(layer), "statekv_reset_layer")
+
+
+def statekv_restore_layer(layer: int, frames_seen: int, count: int) -> None:
+    _check(load_library().statekv_restore_layer(layer, int(frames_seen), int(count)),
+           "statekv_restore_layer")
 
 
 def statekv_free_layer(layer: int) -> None:

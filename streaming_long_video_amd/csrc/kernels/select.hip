@@ -114,6 +114,7 @@ struct SelectJob {
   int ldscores;
   int32_t* sel;           // [Hkv][ldsel] kept pool indices, ascending
   int ldsel;
+  int recent;             // keep the last min(pool, budget) entries (most recent)
 };
 
 struct SumJob {
@@ -174,6 +175,11 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   }
   if (!J.sel) return;  // scores only (per-head rows of the SHARED mode)
   int32_t* out = J.sel + (int64_t)h * J.ldsel;
+  if (J.recent) {  // the pool is in position order: the newest entries are last
+    const int keepn = min(pool, budget);
+    for (int s = tid; s < keepn; s += kSelThreads) out[s] = pool - keepn + s;
+    return;
+  }
   if (pool <= budget) {
     for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
     return;
@@ -310,10 +316,11 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& 
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o, bool shared,
-                         const Stream& st) {
+                         bool recent, const Stream& st) {
+  shared = shared && !recent;  // the recency window is the same for every head
   SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, shared ? nullptr : sel,
-                 ldsel};
-  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel};
+                 ldsel, recent ? 1 : 0};
+  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};
   int sum_blocks = 0;

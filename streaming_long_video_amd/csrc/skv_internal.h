@@ -53,7 +53,7 @@ hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
                          int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o, bool shared,
-                         const Stream& st);
+                         bool recent, const Stream& st);
 
 struct GatherArgs {
   const uint16_t* kc_prev;  // [Hkv][B][D]

@@ -193,7 +193,8 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
                                 p.B, a.S > 1 ? opart : nullptr, a.S,
-                                (int64_t)p.T * p.Hq * p.D, o, shared, ks);
+                                (int64_t)p.T * p.Hq * p.D, o, shared,
+                                (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ks);
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
@@ -203,7 +204,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.kf = a.kf;
     g.vf = a.vf;
     g.sel = at<int32_t>(L, p.off_sel);
-    g.sel_stride = shared ? 0 : p.B;
+    g.sel_stride = (shared && !(p.flags & STATEKV_FLAG_SELECT_RECENT)) ? 0 : p.B;
     g.kc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_ck[nxt]);
     g.vc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_cv[nxt]);
     g.pos_next = at<int64_t>(L, p.off_cpos[nxt]);
@@ -392,6 +393,19 @@ int statekv_reset_layer(statekv_layer* L) {
   return STATEKV_OK;
 }
 
+int statekv_restore_layer(statekv_layer* L, int64_t frames_seen, int32_t count) {
+  if (!L || frames_seen < 0 || count < 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  const int64_t hist = frames_seen * (int64_t)p.T;
+  if (count != (hist < p.B ? hist : (int64_t)p.B)) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!(p.flags & STATEKV_FLAG_D_RING) && hist > p.cap) return STATEKV_ERR_CAPACITY;
+  L->n = frames_seen;
+  L->c = count;
+  L->last_pool = 0;
+  L->mode = frames_seen > 0 ? 1 : 0;
+  return STATEKV_OK;
+}
+
 namespace {
 void destroy_profile_events(statekv_layer* L) {
   for (ProfRecord& r : L->prof) {
@@ -476,7 +490,7 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
-                                       budget, nullptr, 1, 0, nullptr, false, st));
+                                       budget, nullptr, 1, 0, nullptr, false, false, st));
 }
 
 }  // extern "C"

@@ -140,6 +140,35 @@ class Layer:
     def reset(self):
         B.statekv_reset_layer(self.handle)
 
+    def checkpoint(self):
+        """Copies of the layer's resumable state: C rows with positions, the
+        held D rows, frames seen (see restore)."""
+        torch.cuda.synchronize(self.workspace.device)
+        st, dc = self.state(), self.detailed_cache()
+        c, L = st["count"], dc["length"]
+        return {
+            "frames_seen": st["frames_seen"], "count": c,
+            "pos": st["pos"][:, :c].clone(),
+            "k": None if st["k"] is None else st["k"][:, :c].clone(),
+            "v": None if st["v"] is None else st["v"][:, :c].clone(),
+            "d_k": dc["k"][:, :L].clone(), "d_v": dc["v"][:, :L].clone(),
+        }
+
+    def restore(self, ckpt):
+        """Write a checkpoint into this layer's workspace (same configuration)
+        and continue from its next frame."""
+        B.statekv_reset_layer(self.handle)
+        st, dc = self.state(), self.detailed_cache()
+        c, L = ckpt["count"], ckpt["d_k"].shape[1]
+        st["pos"][:, :c].copy_(ckpt["pos"])
+        if st["k"] is not None:
+            st["k"][:, :c].copy_(ckpt["k"])
+            st["v"][:, :c].copy_(ckpt["v"])
+        dc["k"][:, :L].copy_(ckpt["d_k"])
+        dc["v"][:, :L].copy_(ckpt["d_v"])
+        torch.cuda.synchronize(self.workspace.device)
+        B.statekv_restore_layer(self.handle, ckpt["frames_seen"], c)
+
     def close(self):
         if getattr(self, "handle", None):
             B.statekv_free_layer(self.handle)

@@ -263,6 +263,23 @@ def check_rope_and_rounding() -> None:
     got = (so.round_to_bf16(vals).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(got, want), got
 
+
+def check_recency_window() -> None:
+    """Recency rule: the kept set is the B largest positions (closed form); in
+    a stream, after frame n the state holds exactly positions
+    [max(0, (n+1)T - B), (n+1)T)."""
+    pos = np.array([3, 9, 1, 7, 20, 11])
+    assert list(so.select_most_recent(pos, 3)) == [1, 4, 5]
+    assert list(so.select_most_recent(pos, 10)) == [0, 1, 2, 3, 4, 5]
+    rng = np.random.default_rng(5)
+    T, B = 4, 10
+    orc = so.StateKVOracle(2, 1, 8, T, B, recency=True)
+    for n in range(6):
+        r = orc.step(rng.standard_normal((T, 2, 8)), rng.standard_normal((T, 1, 8)),
+                     rng.standard_normal((T, 1, 8)))
+        hi = (n + 1) * T
+        assert list(r.kept_positions[0]) == list(range(max(0, hi - B), hi)), (n, r.kept_positions)
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -273,4 +290,5 @@ ALL_CHECKS = [
     check_selection_and_caches,
     check_decode_attention,
     check_rope_and_rounding,
+    check_recency_window,
 ]

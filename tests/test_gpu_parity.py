@@ -152,6 +152,45 @@ def test_state_kept_as_positions_into_d(flags):
         np.testing.assert_array_equal(snapshot(a).pos[0], snapshot(b).pos[0])
 
 
+@pytest.mark.parametrize("flags", [0, "ring", "c_in_d"])
+def test_checkpoint_and_restore(flags):
+    """A layer checkpointed after 6 frames (C rows and positions, D, frames
+    seen) and restored into a fresh layer continues bit-identically."""
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=12)
+    qs, ks, vs = framegen.stacked_frames(spec, workers=8)
+    f = {0: 0, "ring": skv.STATEKV_FLAG_D_RING, "c_in_d": skv.STATEKV_FLAG_C_IN_D}[flags]
+    cap = (8 if flags == "ring" else 12) * spec.frame_tokens
+    a = _layer(spec, flags=f, detailed_capacity=cap)
+    b = _layer(spec, flags=f, detailed_capacity=cap)
+    for n in range(6):
+        a.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+    b.restore(a.checkpoint())
+    for n in range(6, 12):
+        oa = a.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        ob = b.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        np.testing.assert_array_equal(oa, ob)
+    sa, sb = snapshot(a), snapshot(b)
+    for h in range(spec.n_kv_heads):
+        np.testing.assert_array_equal(sa.pos[h], sb.pos[h])
+        np.testing.assert_array_equal(sa.k[h], sb.k[h])
+
+
+def test_recency_window_mode():
+    """SELECT_RECENT keeps the B most recent candidates (the comparison rule
+    of the pages' App. A.3): teacher-forced against the oracle's recency mode;
+    the state after frame n holds positions [(n+1)T - B, (n+1)T)."""
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=10)
+    frames = framegen.stacked_frames(spec, workers=8)
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SELECT_RECENT)
+    layer, reports, _ = _run_teacher_forced(spec, layer=layer, orc_kw=dict(recency=True),
+                                            frames=frames)
+    _assert_reports(reports, exact_select=True)
+    snap = snapshot(layer)
+    hi = spec.n_frames * spec.frame_tokens
+    for h in range(spec.n_kv_heads):
+        np.testing.assert_array_equal(snap.pos[h], np.arange(hi - spec.state_budget, hi))
+
+
 def test_shared_selection_mode():
     """SHARED: one kept set per layer from the importance summed over all query
     heads; every KV head holds the same positions.  1B-like layer (Hkv = 2),

@@ -143,6 +143,22 @@ def test_rope_configuration_and_argument_errors():
     B.statekv_free_layer(h)
 
 
+def test_restore_argument_errors_are_host_side():
+    cfg = _cfg()  # T = 256, B = 4096, capacity 131072
+    nbytes = B.statekv_workspace_bytes(cfg)
+    h = B.statekv_init_layer(cfg, 1 << 40, nbytes)
+    for args, status in [((-1, 0), -1), ((3, 700), -1), ((20, 4095), -1), ((513, 4096), -4)]:
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_restore_layer(h, *args)
+        assert e.value.status == status, args
+    B.statekv_restore_layer(h, 3, 768)
+    st = B.statekv_state(h)
+    assert st.frames_seen == 3 and st.count == 768 and st.last_pool == 0
+    B.statekv_restore_layer(h, 40, 4096)
+    assert B.statekv_state(h).count == 4096
+    B.statekv_free_layer(h)
+
+
 def test_select_argument_errors():
     with pytest.raises(B.StateKVError):
         B.statekv_select_topb(0, 10, 5, 0)

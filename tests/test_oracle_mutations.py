@@ -200,3 +200,23 @@ def test_rope_pin_catches_mutant(monkeypatch, name, mutant):
     monkeypatch.setattr(so, name, mutant)
     with pytest.raises(AssertionError):
         oracle_pins.check_rope_and_rounding()
+
+
+_orig_recent = so.select_most_recent
+
+
+def recent_keeps_oldest(positions, budget):
+    p = np.asarray(positions)
+    return np.sort(np.argsort(p, kind="stable")[: min(budget, len(p))])
+
+
+def recent_off_by_one(positions, budget):
+    return _orig_recent(positions, max(1, budget - 1))
+
+
+@pytest.mark.parametrize("mutant", [recent_keeps_oldest, recent_off_by_one],
+                         ids=lambda f: f.__name__)
+def test_recency_pin_catches_mutant(monkeypatch, mutant):
+    monkeypatch.setattr(so, "select_most_recent", mutant)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_recency_window()
