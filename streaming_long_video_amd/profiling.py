@@ -34,11 +34,11 @@ import sys
 
 # kernel id -> pattern of its rocprofv3 name (d = 128 instantiations)
 KERNELS = {
-    "attn_stats": r"attn_kernel<128, 1>",
-    "attn_out": r"attn_kernel<128, 2>",
+    "attn_stats": r"attn_kernel<128, 1(, false)?>",
+    "attn_out": r"attn_kernel<128, 2(, false)?>",
     "select": r"select_sum_kernel",
     "gather": r"gather_append_kernel<128>",
-    "full_attn": r"attn_kernel<128, 3>",
+    "full_attn": r"attn_kernel<128, 3(, false)?>",
     "full_combine": r"full_combine_kernel<128>",
     "decode": r"decode_kernel<128>",
 }
