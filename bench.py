@@ -175,7 +175,10 @@ def run_headline(args):
         return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
 
     q_all, k_all, v_all = up(qs), up(ks), up(vs)
-    flags = skv.STATEKV_FLAG_C_IN_D if args.state_layout == "positions" else 0
+    flags = {"rows": 0, "positions": skv.STATEKV_FLAG_C_IN_D,
+             "inplace": skv.STATEKV_FLAG_SLOT_STABLE,
+             "inplace-positions": skv.STATEKV_FLAG_SLOT_STABLE | skv.STATEKV_FLAG_C_IN_D,
+             }[args.state_layout]
     layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T, num_splits=args.splits,
                       flags=flags)
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
@@ -462,8 +465,10 @@ def main(argv=None):
                     help="run a plain device copy of this size before the timed region "
                          "(reference kernel for rocprofv3 byte counters)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = auto)")
-    ap.add_argument("--state-layout", choices=["rows", "positions"], default="rows",
-                    help="C as its own K/V rows (copied on update) or as positions into D")
+    ap.add_argument("--state-layout", choices=["rows", "positions", "inplace", "inplace-positions"],
+                    default="rows",
+                    help="C as its own K/V rows rewritten on update (rows), as positions into "
+                         "D (positions), updated in place (inplace), or both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)

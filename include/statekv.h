@@ -85,7 +85,17 @@ enum {
    * (the rule StateKV is compared against -- rainbus core method: ReKV keeps
    * the last R frames; paperlayer App. A.3 measures the gap).  Importance
    * scores are still computed and reported. */
-  STATEKV_FLAG_SELECT_RECENT = 1u << 4
+  STATEKV_FLAG_SELECT_RECENT = 1u << 4,
+  /* Update C in place: kept state rows stay in their rows, and the kept frame
+   * tokens fill the rows that were freed (evicted rows in ascending row order,
+   * then the unused rows count..B-1 while C fills up; the i-th such row takes
+   * the i-th kept frame token in frame order).  At most T rows per KV head
+   * move instead of every kept row (rainbus method steps: the kept set is
+   * what matters, not its storage order).  C's rows are then in no particular
+   * position order (the state view's pos gives each row's position); ties in
+   * importance still go to the lower original position, as long as the
+   * positions of the tied candidates lie within 2^32 - 3 of the newest one. */
+  STATEKV_FLAG_SLOT_STABLE = 1u << 5
 };
 
 typedef struct statekv_layer statekv_layer; /* opaque, host memory */
@@ -107,9 +117,9 @@ typedef struct statekv_layer_config {
    * hold rotated keys; paperlayer section 3.3: positions stay virtual although
    * C is physically shorter); statekv_rope rotates other tokens (text queries)
    * with the same parameters.  Pairing (x_i, x_{i+d/2}), angle
-   * (p / rope_scaling) * rope_theta^(-2i/d), angles and their cosine and sine
-   * in double precision, the rotation in fp32, the result rounded to bf16
-   * (nearest, ties to even).  rope_theta = 0: q and k arrive rotated.
+   * (p / rope_scaling) * rope_theta^(-2i/d); angle, cosine, sine and the
+   * rotation in double precision, one rounding to bf16 (nearest, ties to
+   * even).  rope_theta = 0: q and k arrive rotated.
    * rope_scaling: linear position interpolation, <= 0 means 1 (the pages
    * require one value for cache building and generation but give none). */
   float rope_theta;
@@ -118,7 +128,8 @@ typedef struct statekv_layer_config {
 
 /* View of the compressed state C_n (borrowed; valid until the next
  * prefill/reset/free on the layer).  Rows [0, count) of every KV head are live,
- * in ascending original position.  Read after synchronising the stream. */
+ * in ascending original position (in any order with SLOT_STABLE).  Read after
+ * synchronising the stream. */
 typedef struct statekv_state_view {
   const void* k;            /* device, [Hkv][capacity][d] bf16                   */
   const void* v;            /* device, [Hkv][capacity][d] bf16                   */
@@ -215,7 +226,8 @@ int statekv_reset_layer(statekv_layer* layer);
  * layer after frame n-1 is (C_n rows with their positions, D[0 : n*T), n):
  * the caller writes them into the regions that statekv_state and
  * statekv_detailed_cache report (C rows [0, count) of k, v and pos in
- * ascending position; D as the detailed view lays it out), then calls this
+ * ascending position, any order with SLOT_STABLE; D as the detailed view lays
+ * it out), then calls this
  * so that the next statekv_prefill_frame processes frame frames_seen.
  * count must equal min(B, frames_seen * T) (STATEKV_ERR_INVALID_ARGUMENT
  * otherwise), and a linear D must hold frames_seen * T tokens

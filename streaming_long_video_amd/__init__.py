@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     STATEKV_FLAG_NONCAUSAL_FRAME,
     STATEKV_FLAG_SELECT_RECENT,
     STATEKV_FLAG_SELECT_SHARED,
+    STATEKV_FLAG_SLOT_STABLE,
     STATEKV_KERNELS,
     StateKVError,
     load_library,

@@ -28,6 +28,7 @@ STATEKV_FLAG_D_RING = 1 << 1
 STATEKV_FLAG_NONCAUSAL_FRAME = 1 << 2
 STATEKV_FLAG_C_IN_D = 1 << 3
 STATEKV_FLAG_SELECT_RECENT = 1 << 4
+STATEKV_FLAG_SLOT_STABLE = 1 << 5
 
 
 class StateKVError(RuntimeError):

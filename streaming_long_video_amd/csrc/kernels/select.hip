@@ -17,6 +17,15 @@
 // first k keys of the boundary bin in pool order, compacted with one
 // workgroup scan so the output lists pool indices in ascending order.  Only
 // integer operations decide the result: exact and deterministic.
+//
+// With the in-place (slot-stable) state update the state rows are in no
+// position order.  Exact ties at the boundary are then broken by a second
+// radix select over keys that rank the tied candidates by age (older = lower
+// position = preferred) above everything dropped and below everything kept
+// outright; the output is the list of rows to refill (evicted rows in row
+// order, then the unused rows while C fills) and the kept frame tokens in
+// frame order.  The recency window ranks the candidates by position the same
+// way.
 #include "../skv_internal.h"
 
 namespace skv {
@@ -115,6 +124,7 @@ struct SelectJob {
   int32_t* sel;           // [Hkv][ldsel] kept pool indices, ascending
   int ldsel;
   int recent;             // keep the last min(pool, budget) entries (most recent)
+  InPlace ip;             // ip.pos null: the pool is in position order
 };
 
 struct SumJob {
@@ -175,73 +185,120 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   }
   if (!J.sel) return;  // scores only (per-head rows of the SHARED mode)
   int32_t* out = J.sel + (int64_t)h * J.ldsel;
-  if (J.recent) {  // the pool is in position order: the newest entries are last
+  const bool in_place = J.ip.pos != nullptr;
+  if (pool <= budget) {  // nothing is dropped
+    if (!in_place)
+      for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
+    return;  // in place, the frame is simply appended
+  }
+  if (J.recent && !in_place) {  // the pool is in position order: the newest entries are last
     const int keepn = min(pool, budget);
     for (int s = tid; s < keepn; s += kSelThreads) out[s] = pool - keepn + s;
     return;
   }
-  if (pool <= budget) {
-    for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
-    return;
+  // age of pool entry j in positions (0: the frame's last token), clamped so
+  // that 1 + age fits below the all-ones key
+  const int64_t* hpos = in_place ? J.ip.pos + (int64_t)h * J.ip.ldpos : nullptr;
+  const int64_t newest = J.ip.frame_pos0 + J.ip.T - 1;
+  auto age = [&](int j) -> uint32_t {
+    const int64_t p = j < J.ip.c ? hpos[j] : J.ip.frame_pos0 + (j - J.ip.c);
+    const uint64_t a = (uint64_t)(newest - p);
+    return a < 0xFFFFFFFDull ? (uint32_t)a : 0xFFFFFFFDu;
+  };
+  if (J.recent) {  // in place: rank by position, newest first (same thread owns key j)
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+    for (int j = tid; j < pool; j += kSelThreads) {
+      const uint32_t u = 0xFFFFFFFEu - age(j);
+      keys[j] = u;
+      mn = min(mn, u);
+      mx = max(mx, u);
+    }
   }
   // the first pass's histogram starts cleared (the min/max barrier orders it)
   for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[0][0][0])[i] = 0u;
   uint32_t kmax;
-  const uint32_t kmin = block_min_max(mn, mx, red, &kmax);  // also orders keys[] writes
+  uint32_t kmin = block_min_max(mn, mx, red, &kmax);  // also orders keys[] writes
 
-  // radix select below the common prefix of all keys; histograms and the
-  // boundary record alternate between two buffers so that a pass needs
-  // three barriers
-  uint32_t prefix = kmin, pmask = 0xFFFFFFFFu;
-  uint32_t k = (uint32_t)budget;  // rank (from the top) still to place
-  int hb = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
-  if (hb >= 0) {
-    pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
-    prefix = kmin & pmask;
-  }
-  int buf = 0;
   const int lane = tid & 63;
-  while (hb >= 0) {
-    const int shift = hb >= 7 ? hb - 7 : 0;
-    const uint32_t dmask = (2u << (hb - shift)) - 1u;  // digit bits [shift, hb]
+  int buf = 0;  // whist[buf] is clear whenever a radix select starts
+  uint32_t prefix, pmask, k;
+  // radix select below the common prefix of all keys; histograms and the
+  // boundary record alternate between two buffers so that a pass needs three
+  // barriers.  Returns the boundary bin's size; k is then the number of its
+  // keys to keep.
+  auto radix = [&]() -> uint32_t {
+    prefix = kmin;
+    pmask = 0xFFFFFFFFu;
+    k = (uint32_t)budget;  // rank (from the top) still to place
+    int hb = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
+    if (hb >= 0) {
+      pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+      prefix = kmin & pmask;
+    }
+    uint32_t bin = (uint32_t)pool;
+    while (hb >= 0) {
+      const int shift = hb >= 7 ? hb - 7 : 0;
+      const uint32_t dmask = (2u << (hb - shift)) - 1u;  // digit bits [shift, hb]
+      for (int j = tid; j < pool; j += kSelThreads) {
+        const uint32_t u = keys[j];
+        if ((u & pmask) == prefix) {
+          const uint32_t dig = (u >> shift) & dmask;
+          atomicAdd(&whist[buf][w][dig >> 1], 1u << ((dig & 1u) * 16u));
+        }
+      }
+      for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[buf ^ 1][0][0])[i] = 0u;
+      __syncthreads();
+      // digits in descending order over threads 0..255 (waves 0..3)
+      const uint32_t d = 255u - (uint32_t)tid;
+      uint32_t cnt = 0, incl = 0;
+      if (tid < 256) {
+        if (d <= dmask) {
+#pragma unroll
+          for (int i = 0; i < kSelWaves; ++i) cnt += (whist[buf][i][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu;
+        }
+        incl = wave_inclusive_sum(cnt);
+        if (lane == 63) wtot[w] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t excl = incl - cnt;
+        for (int i = 0; i < w; ++i) excl += wtot[i];
+        if (cnt && excl < k && k <= excl + cnt) {
+          found[buf][0] = d;
+          found[buf][1] = excl;
+          found[buf][2] = cnt;
+        }
+      }
+      __syncthreads();
+      prefix |= found[buf][0] << shift;
+      pmask |= dmask << shift;
+      k -= found[buf][1];
+      bin = found[buf][2];
+      if (bin == k) {  // the whole boundary bin is kept: no tie to break
+        buf ^= 1;  // whist[buf ^ 1] was cleared during this pass
+        break;
+      }
+      hb = shift - 1;
+      buf ^= 1;
+    }
+    return bin;
+  };
+  uint32_t bin = radix();
+  if (in_place && bin > k) {
+    // exact ties at the boundary (every key bit resolved): keep the k oldest
+    // of them, by a second select over 0 (dropped) < 1 + age (tied) < ~0 (kept)
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
     for (int j = tid; j < pool; j += kSelThreads) {
       const uint32_t u = keys[j];
-      if ((u & pmask) == prefix) {
-        const uint32_t dig = (u >> shift) & dmask;
-        atomicAdd(&whist[buf][w][dig >> 1], 1u << ((dig & 1u) * 16u));
-      }
+      const uint32_t v = u > prefix ? 0xFFFFFFFFu : u < prefix ? 0u : 1u + age(j);
+      keys[j] = v;
+      mn = min(mn, v);
+      mx = max(mx, v);
     }
-    for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[buf ^ 1][0][0])[i] = 0u;
-    __syncthreads();
-    // digits in descending order over threads 0..255 (waves 0..3)
-    const uint32_t d = 255u - (uint32_t)tid;
-    uint32_t cnt = 0, incl = 0;
-    if (tid < 256) {
-      if (d <= dmask) {
-#pragma unroll
-        for (int i = 0; i < kSelWaves; ++i) cnt += (whist[buf][i][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu;
-      }
-      incl = wave_inclusive_sum(cnt);
-      if (lane == 63) wtot[w] = incl;
-    }
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t excl = incl - cnt;
-      for (int i = 0; i < w; ++i) excl += wtot[i];
-      if (cnt && excl < k && k <= excl + cnt) {
-        found[buf][0] = d;
-        found[buf][1] = excl;
-        found[buf][2] = cnt;
-      }
-    }
-    __syncthreads();
-    prefix |= found[buf][0] << shift;
-    pmask |= dmask << shift;
-    k -= found[buf][1];
-    const uint32_t bin = found[buf][2];
-    if (bin == k) break;  // the whole boundary bin is kept: no tie to break
-    hb = shift - 1;
-    buf ^= 1;
+    kmin = block_min_max(mn, mx, red, &kmax);
+    bin = radix();
   }
 
   // keep (u & pmask) > prefix, and the first k keys with (u & pmask) == prefix
@@ -255,17 +312,49 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   }
   const uint32_t packed = block_exclusive_scan(ngt | (neq << 16), red, nullptr);
   const uint32_t gt_before = packed & 0xFFFFu, eq_before = packed >> 16;
-  uint32_t slot = gt_before + min(eq_before, k);
-  uint32_t eqr = eq_before;
-  for (int j = j0; j < j1; ++j) {
+  if (!in_place) {
+    uint32_t slot = gt_before + min(eq_before, k);
+    uint32_t eqr = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = keys[j] & pmask;
+      if (u > prefix) {
+        out[slot++] = j;
+      } else if (u == prefix) {
+        if (eqr < k) out[slot++] = j;
+        ++eqr;
+      }
+    }
+    return;
+  }
+  // in place: rows to refill and the kept frame tokens, both ascending
+  const int c = J.ip.c, T = J.ip.T;
+  auto kept = [&](int j, uint32_t& eqr) -> bool {
     const uint32_t u = keys[j] & pmask;
-    if (u > prefix) {
-      out[slot++] = j;
-    } else if (u == prefix) {
-      if (eqr < k) out[slot++] = j;
-      ++eqr;
+    if (u > prefix) return true;
+    if (u < prefix) return false;
+    return eqr++ < k;
+  };
+  uint32_t nev = 0u, nkf = 0u, eqr = eq_before;
+  for (int j = j0; j < j1; ++j) {
+    const bool keep = kept(j, eqr);
+    if (j < c) nev += !keep;
+    else nkf += keep;
+  }
+  uint32_t tot;
+  const uint32_t packed2 = block_exclusive_scan(nev | (nkf << 16), red, &tot);
+  uint32_t e = packed2 & 0xFFFFu, f = packed2 >> 16;
+  eqr = eq_before;
+  for (int j = j0; j < j1; ++j) {
+    const bool keep = kept(j, eqr);
+    if (j < c) {
+      if (!keep) out[e++] = j;
+    } else if (keep) {
+      out[T + f++] = j - c;
     }
   }
+  const uint32_t evicted = tot & 0xFFFFu;
+  for (int r = tid; r < budget - c; r += kSelThreads) out[evicted + r] = c + r;
+  if (tid == 0) out[2 * T] = (int32_t)(tot >> 16);
 }
 
 // Blocks [0, n_select) handle one KV head each (scores, and the selection
@@ -316,11 +405,12 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& 
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o, bool shared,
-                         bool recent, const Stream& st) {
+                         bool recent, const InPlace& ip, const Stream& st) {
   shared = shared && !recent;  // the recency window is the same for every head
   SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, shared ? nullptr : sel,
-                 ldsel, recent ? 1 : 0};
-  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0};
+                 ldsel, recent ? 1 : 0, ip};
+  // the layer-wide job: every head holds the same rows, so head 0's positions serve
+  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};
   int sum_blocks = 0;

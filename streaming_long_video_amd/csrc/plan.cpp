@@ -24,7 +24,7 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (cfg->num_splits < 0) return STATEKV_ERR_INVALID_ARGUMENT;
   if (cfg->flags & ~(uint32_t)(STATEKV_FLAG_SELECT_SHARED | STATEKV_FLAG_D_RING |
                                STATEKV_FLAG_NONCAUSAL_FRAME | STATEKV_FLAG_C_IN_D |
-                               STATEKV_FLAG_SELECT_RECENT))
+                               STATEKV_FLAG_SELECT_RECENT | STATEKV_FLAG_SLOT_STABLE))
     return STATEKV_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & STATEKV_FLAG_C_IN_D) && (cfg->flags & STATEKV_FLAG_D_RING))
     return STATEKV_ERR_UNSUPPORTED;
@@ -87,10 +87,13 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   const size_t c_rows = (size_t)Hkv * B;
   const size_t d_rows = (size_t)Hkv * (size_t)q.cap;
   const size_t c_kv = (cfg->flags & STATEKV_FLAG_C_IN_D) ? 0 : c_rows * D * 2;
+  // two state buffers (ping-pong), one when the state is updated in place
+  const bool in_place = cfg->flags & STATEKV_FLAG_SLOT_STABLE;
   for (int i = 0; i < 2; ++i) {
-    q.off_ck[i] = off; off = align_up(off + c_kv, A);
-    q.off_cv[i] = off; off = align_up(off + c_kv, A);
-    q.off_cpos[i] = off; off = align_up(off + c_rows * 8, A);
+    const size_t rows = (i == 1 && in_place) ? 0 : c_rows;
+    q.off_ck[i] = off; off = align_up(off + (rows ? c_kv : 0), A);
+    q.off_cv[i] = off; off = align_up(off + (rows ? c_kv : 0), A);
+    q.off_cpos[i] = off; off = align_up(off + rows * 8, A);
   }
   q.off_dk = off; off = align_up(off + d_rows * D * 2, A);
   q.off_dv = off; off = align_up(off + d_rows * D * 2, A);
@@ -101,7 +104,10 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   q.off_o = off; off = align_up(off + opart * T * Hq * D * 4, A);
   q.off_sig = off; off = align_up(off + (size_t)Hkv * q.rt * q.ldsig * 4, A);
   q.off_scores = off; off = align_up(off + (size_t)Hkv * q.ldsig * 4, A);
-  q.off_sel = off; off = align_up(off + (size_t)Hkv * B * 4, A);
+  // selection rows: kept pool indices, or with the in-place update the move
+  // lists (freed rows [0, T), frame tokens [T, 2T), move count at 2T)
+  q.ldsel = in_place ? (B > 2 * T + 1 ? B : 2 * T + 1) : B;
+  q.off_sel = off; off = align_up(off + (size_t)Hkv * q.ldsel * 4, A);
   const bool rope = q.rope_theta > 0.0;
   q.off_qrot = off; off = align_up(off + (rope ? (size_t)T * Hq * D * 2 : 0), A);
   q.off_krot = off; off = align_up(off + (rope ? (size_t)T * Hkv * D * 2 : 0), A);

@@ -38,6 +38,7 @@ struct Plan {
   int32_t ldsig;      // row stride (floats) of score partials / scores
   int32_t full_splits;  // key splits of the full-attention baseline
   int32_t part_splits;  // largest of the split counts: partial buffers sized for it
+  int32_t ldsel;      // row stride (int32) of the selection region
   // workspace offsets (bytes, 256-aligned)
   size_t off_ck[2], off_cv[2], off_cpos[2];
   size_t off_dk, off_dv;

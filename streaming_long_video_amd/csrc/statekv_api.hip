@@ -150,13 +150,14 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   const bool ring = p.flags & STATEKV_FLAG_D_RING;
   const bool shared = p.flags & STATEKV_FLAG_SELECT_SHARED;
   const bool c_in_d = p.flags & STATEKV_FLAG_C_IN_D;
+  const bool in_place = p.flags & STATEKV_FLAG_SLOT_STABLE;
   const int64_t next_len = (L->n + 1) * (int64_t)p.T;
   if (!ring && next_len > p.cap) return STATEKV_ERR_CAPACITY;
   if (L->n * (int64_t)p.T + p.T + p.offset > ((int64_t)1 << 62)) return STATEKV_ERR_CAPACITY;
   hipStream_t st = static_cast<hipStream_t>(stream);
   L->mode = 1;
 
-  const int cur = L->cur, nxt = cur ^ 1;
+  const int cur = L->cur, nxt = in_place ? cur : cur ^ 1;
   const int c = L->c;
   const int pool = c + p.T;
   const int newc = pool < p.B ? pool : p.B;
@@ -188,13 +189,21 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
               [&](const skv::Stream& ks) { return skv::launch_attn_stats(a1, p.D, ks); });
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&](const skv::Stream& ks) { return skv::launch_attn_out(a, p.D, ks); });
+  skv::InPlace ip = {};
+  if (in_place) {
+    ip.pos = at<int64_t>(L, p.off_cpos[cur]);
+    ip.ldpos = p.B;
+    ip.c = c;
+    ip.T = p.T;
+    ip.frame_pos0 = p.offset + L->n * (int64_t)p.T;
+  }
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_SELECT, st, [&](const skv::Stream& ks) {
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
-                                p.B, a.S > 1 ? opart : nullptr, a.S,
+                                p.ldsel, a.S > 1 ? opart : nullptr, a.S,
                                 (int64_t)p.T * p.Hq * p.D, o, shared,
-                                (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ks);
+                                (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ip, ks);
     });
   if (e == hipSuccess) {
     skv::GatherArgs g = {};
@@ -204,7 +213,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.kf = a.kf;
     g.vf = a.vf;
     g.sel = at<int32_t>(L, p.off_sel);
-    g.sel_stride = (shared && !(p.flags & STATEKV_FLAG_SELECT_RECENT)) ? 0 : p.B;
+    g.sel_stride = (shared && !(p.flags & STATEKV_FLAG_SELECT_RECENT)) ? 0 : p.ldsel;
     g.kc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_ck[nxt]);
     g.vc_next = c_in_d ? nullptr : at<uint16_t>(L, p.off_cv[nxt]);
     g.pos_next = at<int64_t>(L, p.off_cpos[nxt]);
@@ -220,6 +229,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.newc = newc;
     g.keep_all = pool <= p.B;
     g.ring = ring;
+    g.in_place = in_place;
     e = timed(L, STATEKV_KERNEL_GATHER, st,
               [&](const skv::Stream& ks) { return skv::launch_gather_append(g, p.D, ks); });
   }
@@ -490,7 +500,8 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
-                                       budget, nullptr, 1, 0, nullptr, false, false, st));
+                                       budget, nullptr, 1, 0, nullptr, false, false,
+                                       skv::InPlace{}, st));
 }
 
 }  // extern "C"

@@ -108,6 +108,21 @@ int main() {
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
   c.flags = STATEKV_FLAG_SELECT_SHARED;
   CHECK(skv::make_plan(&c, &p) == STATEKV_OK);
+  {
+    // in-place update: one state buffer, selection rows wide enough for the
+    // move lists (2T + 1 when that exceeds B)
+    skv::Plan a, b;
+    c.flags = 0;
+    CHECK(skv::make_plan(&c, &a) == STATEKV_OK && a.ldsel == 4096);
+    c.flags = STATEKV_FLAG_SLOT_STABLE;
+    CHECK(skv::make_plan(&c, &b) == STATEKV_OK && b.ldsel == 4096);
+    CHECK(a.total - b.total >= (size_t)4 * 4096 * (128 * 2 * 2 + 8));
+    CHECK(b.off_ck[1] == b.off_cv[1] && b.off_cv[1] == b.off_cpos[1]);
+    statekv_layer_config s = cfg(4, 2, 64, 300, 100, 3000);
+    s.flags = STATEKV_FLAG_SLOT_STABLE;
+    CHECK(skv::make_plan(&s, &b) == STATEKV_OK && b.ldsel == 601);
+    CHECK(b.off_qrot - b.off_sel >= (size_t)2 * 601 * 4);
+  }
   c.flags = 0;
   c.num_splits = 3;
   CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 3 && p.stat_splits == 3);

@@ -9,6 +9,8 @@ from typing import List, Optional
 import numpy as np
 import torch
 
+from oracle import select_most_recent, select_top_b
+
 # Acceptance bounds for the attention output (fp32 O against the float64
 # oracle, both fed identical bf16 inputs).
 O_MAXABS = 2e-2
@@ -64,6 +66,29 @@ def snapshot(layer) -> StateSnapshot:
                          [v[h] for h in range(H)], [sc[h] for h in range(H)], pool)
 
 
+# layer flags the helpers look at (values of include/statekv.h)
+FLAG_SELECT_SHARED = 1 << 0
+FLAG_SELECT_RECENT = 1 << 4
+FLAG_SLOT_STABLE = 1 << 5
+
+
+def expected_in_place_rows(prev_rows, kept_positions, frame_positions, budget):
+    """Row layout of C after the in-place (slot-stable) update: rows whose
+    position is kept stay put; the freed rows -- rows whose position was
+    dropped, in row order, then the unused rows len(prev_rows)..budget-1 --
+    take the kept frame tokens in frame order."""
+    kept = set(int(p) for p in kept_positions)
+    c = len(prev_rows)
+    new_len = min(budget, c + len(frame_positions))
+    rows = [int(p) for p in prev_rows] + [None] * (new_len - c)
+    free = [r for r in range(c) if rows[r] not in kept] + list(range(c, new_len))
+    incoming = [int(p) for p in frame_positions if int(p) in kept]
+    assert len(free) == len(incoming), (len(free), len(incoming))
+    for r, p in zip(free, incoming):
+        rows[r] = p
+    return np.array(rows, dtype=np.int64)
+
+
 @dataclasses.dataclass
 class FrameReport:
     n: int
@@ -75,7 +100,13 @@ class FrameReport:
 
 
 def teacher_forced_frame(orc, layer, n, q, k, v, o_gpu_dev=None) -> FrameReport:
-    """Run GPU frame n and the oracle step from the GPU's C_{n-1}; compare."""
+    """Run GPU frame n and the oracle step from the GPU's C_{n-1}; compare.
+
+    Besides the errors against the oracle, the GPU's kept set must be exactly
+    the oracle's selection rule applied to the GPU's own fp32 scores (per-head
+    rule; the recency rule on positions), and the state rows must be in
+    ascending position, or with SLOT_STABLE in the in-place layout."""
+    flags = getattr(layer, "flags", 0)
     before = snapshot(layer)
     orc.load_state(n, before.pos, before.k, before.v)
     q_d, k_d, v_d = to_dev(q), to_dev(k), to_dev(v)
@@ -83,18 +114,35 @@ def teacher_forced_frame(orc, layer, n, q, k, v, o_gpu_dev=None) -> FrameReport:
     after = snapshot(layer)
     ref = orc.step(q, k, v)
     maxabs, relrms = o_errors(o.cpu().numpy(), ref.o)
+    frame_pos = layer.position_offset + n * q.shape[0] + np.arange(q.shape[0], dtype=np.int64)
     score_err = 0.0
     match = total = 0
     for h in range(len(ref.scores)):
         np.testing.assert_array_equal(ref.pool_positions[h].shape[0], after.pool)
+        # the GPU's pool is [its state rows as held ; frame]; the oracle's ascends
+        gpu_pool = np.concatenate([before.pos[h], frame_pos])
+        order = np.argsort(gpu_pool, kind="stable")
+        np.testing.assert_array_equal(gpu_pool[order], ref.pool_positions[h])
         s_ref = ref.scores[h]
-        s_gpu = after.scores[h].astype(np.float64)
+        s_gpu = after.scores[h].astype(np.float64)[order]
         score_err = max(score_err, float((np.abs(s_gpu - s_ref) /
                                           (SCORE_ATOL + SCORE_RTOL * np.abs(s_ref))).max()))
         kept_ref = set(ref.kept_positions[h].tolist())
         kept_gpu = after.pos[h].tolist()
-        assert kept_gpu == sorted(kept_gpu), "state positions must ascend"
         assert len(kept_gpu) == len(kept_ref)
+        if flags & FLAG_SELECT_RECENT:
+            rule = gpu_pool[select_most_recent(gpu_pool, layer.B)]
+        elif not flags & FLAG_SELECT_SHARED:
+            rule = gpu_pool[select_top_b(after.scores[h].astype(np.float64), gpu_pool, layer.B)]
+        else:
+            rule = None  # the layer-wide sum is not one of the per-head rows
+        if rule is not None:
+            assert sorted(kept_gpu) == sorted(rule.tolist()), (n, h, "selection rule")
+        if flags & FLAG_SLOT_STABLE:
+            np.testing.assert_array_equal(
+                after.pos[h], expected_in_place_rows(before.pos[h], kept_gpu, frame_pos, layer.B))
+        else:
+            assert kept_gpu == sorted(kept_gpu), "state positions must ascend"
         match += len(kept_ref.intersection(kept_gpu))
         total += len(kept_ref)
     return FrameReport(n, maxabs, relrms, score_err, match, total)
@@ -117,8 +165,9 @@ def check_caches_bitwise(layer, frames_k, frames_v, n_frames: Optional[int] = No
     np.testing.assert_array_equal(dk, np.transpose(K, (1, 0, 2)))
     np.testing.assert_array_equal(dv, np.transpose(V, (1, 0, 2)))
     pos = st["pos"][:, :c].cpu().numpy()
+    in_place = getattr(layer, "flags", 0) & FLAG_SLOT_STABLE
     for h in range(pos.shape[0]):
-        assert np.all(np.diff(pos[h]) > 0)
+        assert np.all(np.diff(np.sort(pos[h]) if in_place else pos[h]) > 0)
     if st["k"] is None:  # C kept as positions into D: nothing else to compare
         return
     ck = to_bits(st["k"][:, :c])

@@ -220,6 +220,68 @@ def test_shared_selection_mode():
     assert match >= SELECT_AGREEMENT * total, (match, total)
 
 
+@pytest.mark.parametrize("mode", ["plain", "shared", "c_in_d", "recent"])
+def test_in_place_state_update(mode):
+    """SLOT_STABLE: kept state rows stay where they are and the kept frame
+    tokens fill the freed rows.  1B-like layer, 24 frames: teacher-forced
+    against the oracle (the helper checks the exact row layout and the
+    selection rule on the GPU's own scores), then free running beside the
+    default layout on the same stream (same outputs up to the summation order
+    of the state rows, same kept sets up to near-ties)."""
+    spec = framegen.workload("internvl3_1b_layer").replace(n_frames=24)
+    frames = framegen.stacked_frames(spec, workers=8)
+    qs, ks, vs = frames
+    extra = {"plain": 0, "shared": skv.STATEKV_FLAG_SELECT_SHARED,
+             "c_in_d": skv.STATEKV_FLAG_C_IN_D, "recent": skv.STATEKV_FLAG_SELECT_RECENT}[mode]
+    f = skv.STATEKV_FLAG_SLOT_STABLE | extra
+    orc_kw = dict(shared=mode == "shared", recency=mode == "recent")
+    layer, reports, _ = _run_teacher_forced(spec, layer=_layer(spec, flags=f), orc_kw=orc_kw,
+                                            frames=frames)
+    _assert_reports(reports, exact_select=mode == "recent")
+    check_caches_bitwise(layer, ks, vs)
+    a = _layer(spec, flags=f)
+    b = _layer(spec, flags=extra)
+    match = total = 0
+    for n in range(spec.n_frames):
+        oa = a.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        ob = b.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n])).cpu().numpy()
+        maxabs, relrms = o_errors(oa, ob.astype(np.float64))
+        assert maxabs <= O_MAXABS and relrms <= O_RELRMS, (n, maxabs, relrms)
+        sa, sb = snapshot(a), snapshot(b)
+        for h in range(spec.n_kv_heads):
+            match += len(set(sa.pos[h].tolist()).intersection(sb.pos[h].tolist()))
+            total += len(sb.pos[h])
+    print(f"in-place vs row layout, kept-set agreement {match / total:.6f}")
+    assert match >= SELECT_AGREEMENT * total, (match, total)
+
+
+def test_in_place_ties_go_to_lower_positions():
+    """Keys drawn from four vectors make whole groups of state tokens tie
+    exactly (identical logits, identical column sums); with the in-place
+    layout the state rows are out of position order, so the kept members of
+    a tied group must be found by position.  Teacher-forced: the kept set is
+    the oracle's rule on the GPU's own scores and the oracle's kept set."""
+    Hq, Hkv, d, T, B, N = 4, 1, 64, 32, 48, 12
+    spec = framegen.FrameSpec(Hq, Hkv, d, T, N, B, 1e4, 5, sinks=False)
+    qs, ks, vs = framegen.stacked_frames(spec, workers=4)
+    rng = np.random.default_rng(123)
+    basis = framegen.f64_to_bf16_bits(rng.standard_normal((4, d)))
+    ks = basis[rng.integers(0, 4, size=(N, T, Hkv))]
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SLOT_STABLE)
+    orc = _oracle(spec)
+    tied_frames = 0
+    for n in range(N):
+        r = teacher_forced_frame(orc, layer, n, qs[n], ks[n], vs[n])
+        assert r.kept_match == r.kept_total, r
+        assert r.maxabs <= O_MAXABS and r.relrms <= O_RELRMS, r
+        after = snapshot(layer)
+        if after.pool > B:
+            s = np.sort(after.scores[0])[::-1]
+            tied_frames += int(s[B - 1] == s[B])  # a tie straddles the boundary
+    print(f"frames with a tie across the budget boundary: {tied_frames}")
+    assert tied_frames >= 3
+
+
 @pytest.mark.parametrize("shape", [
     # (Hq, Hkv, d, T, B, frames): ragged T, B not a tile multiple, G=1, G=16, T=1
     (6, 2, 128, 17, 50, 6),

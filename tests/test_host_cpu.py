@@ -5,6 +5,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -65,6 +66,41 @@ def test_workspace_bytes_and_validation():
     with pytest.raises(B.StateKVError) as e:
         B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_C_IN_D | B.STATEKV_FLAG_D_RING))
     assert e.value.status == -2
+    # in-place update: one compressed state instead of two
+    m = B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_SLOT_STABLE))
+    assert m <= n - 4 * 4096 * (128 * 2 * 2 + 8)
+    assert B.statekv_workspace_bytes(_cfg(flags=0b110111)) > 0  # all but C_IN_D
+
+
+def test_in_place_layout_rule():
+    """The row layout the GPU tests expect from the in-place update: a worked
+    case, then invariants on random cases (kept rows unmoved, the rows hold
+    exactly the kept set, frame tokens enter freed rows in frame order)."""
+    from gpu_util import expected_in_place_rows
+    # rows hold positions 5, 1, 9, 3; frame 10..13; keep {1, 3, 11, 13}; B = 4
+    rows = expected_in_place_rows([5, 1, 9, 3], [1, 3, 11, 13], [10, 11, 12, 13], 4)
+    assert rows.tolist() == [11, 1, 13, 3]
+    # filling up: rows 0..1 live, B = 5, frame of 4, keep {0, 2, 3, 4, 5}
+    rows = expected_in_place_rows([0, 1], [0, 2, 3, 4, 5], [2, 3, 4, 5], 5)
+    assert rows.tolist() == [0, 2, 3, 4, 5]
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        c, T, Bud = int(rng.integers(0, 12)), int(rng.integers(1, 8)), int(rng.integers(1, 14))
+        c = min(c, Bud)
+        prev = rng.permutation(50)[:c]
+        frame = 50 + np.arange(T)
+        pool = np.concatenate([prev, frame])
+        keep = rng.permutation(pool)[: min(Bud, c + T)]
+        if c + T > Bud and len(keep) < Bud:
+            continue
+        rows = expected_in_place_rows(prev, keep, frame, Bud)
+        assert sorted(rows.tolist()) == sorted(keep.tolist())
+        for r in range(c):
+            if prev[r] in keep:
+                assert rows[r] == prev[r]
+        incoming = [p for p in rows.tolist() if p >= 50]
+        freed = [r for r in range(len(rows)) if rows[r] >= 50]
+        assert incoming == sorted(incoming) and freed == sorted(freed)
 
 
 def test_init_views_and_argument_errors_are_host_side():
