@@ -78,16 +78,16 @@ def useful_attention_flops(Hq, d, T, c) -> float:
     return 4.0 * Hq * d * visible_pairs(T, c)
 
 
-def gather_bytes(Hkv, d, T, B, c) -> float:
+def gather_bytes(Hkv, d, T, B, c, rows=True) -> float:
     """C_n gather + D append, bytes that must cross HBM once.
 
     Per kept row: read K and V (2*d*2 bytes) from C_{n-1} or the frame, write
-    them to C_n; read the selection index (4 B) and the old position (8 B),
-    write the position (8 B).  Append: read the frame's K and V rows, write
-    them to D."""
+    them to C_n (not when C is kept as positions into D); read the selection
+    index (4 B) and the old position (8 B), write the position (8 B).  Append:
+    read the frame's K and V rows, write them to D."""
     newc = min(B, c + T)
     row = 2 * d * 2
-    gather = Hkv * newc * (2 * row + 4 + 8 + 8)
+    gather = Hkv * newc * ((2 * row if rows else 0) + 4 + 8 + 8)
     append = Hkv * T * 2 * row
     return float(gather + append)
 
@@ -268,7 +268,8 @@ def run_headline(args):
             "executed_frac_of_peak": 1.5 * useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
         }
     if breakdown_us.get("gather"):
-        gb = float(np.mean([gather_bytes(Hkv, d, T, Bs, c) for c in cs]))
+        gb = float(np.mean([gather_bytes(Hkv, d, T, Bs, c, rows=args.state_layout == "rows")
+                            for c in cs]))
         tg = breakdown_us["gather"]
         result["gather_append"] = {
             "bytes_per_launch": gb, "avg_launch_us": tg,

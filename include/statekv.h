@@ -174,7 +174,8 @@ int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace,
  * frame n = frames_seen: reads q/k/v, writes o, updates C and D, and advances
  * frames_seen.  Kernels: attention statistics pass, attention output + score
  * pass, top-B select (with the split-O reduction in the same launch),
- * gather + detailed-cache append. */
+ * gather + detailed-cache append (with SLOT_STABLE the select launch applies
+ * the state update and the append itself: three launches). */
 int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
                           const void* v, float* o, void* stream);
 
@@ -248,8 +249,11 @@ enum {
   STATEKV_KERNEL_SPLIT_SUM = 2,  /* split combine of the full-attention baseline
                                     and of decoding (the StateKV path sums its
                                     split O partials in the SELECT launch)      */
-  STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select + O split sum */
-  STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append         */
+  STATEKV_KERNEL_SELECT = 3,     /* importance sums + top-B select + O split sum
+                                    (with SLOT_STABLE also the state moves and
+                                    the detailed-cache append)                  */
+  STATEKV_KERNEL_GATHER = 4,     /* C_n gather + detailed-cache append (not
+                                    launched with SLOT_STABLE)                  */
   STATEKV_KERNEL_DECODE = 5,     /* decoding over D: split partials            */
   STATEKV_KERNEL_ROPE = 6,       /* in-library rotary embedding of the frame   */
   STATEKV_NUM_KERNELS = 7

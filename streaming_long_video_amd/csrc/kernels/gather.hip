@@ -7,9 +7,6 @@
 //     candidates of previous state plus frame become the new compressed state;
 //     paperlayer.ai section 3.3: virtual positions are kept although the
 //     state is physically shorter);
-//   in place (slot-stable): C[h][row_i] = frame token t_i for the move list
-//     (row_i, t_i), i < moves, that the selection wrote: kept state rows stay
-//     where they are, at most T rows move;
 //   append: D[h][slot(p)] = frame token p for every token of the frame
 //     (rainbus method steps: after frame n the frame's keys/values join the
 //     detailed state, which keeps every video token for decoding).
@@ -35,47 +32,6 @@ __global__ __launch_bounds__(kCopyThreads) void gather_append_kernel(GatherArgs 
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   u32x4 buf[PER];
-  if (b < gather_blocks && g.in_place) {
-    const int per_h = (g.T + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int h = b / per_h;
-    const int s0 = (b % per_h) * kRowsPerBlock;
-    const int32_t* sel = g.sel + (int64_t)h * g.sel_stride;
-    const int moves = g.keep_all ? g.T : min(max(sel[2 * g.T], 0), g.T);
-    const int rows = min(kRowsPerBlock, moves - s0);
-    if (rows <= 0) return;
-    auto dst_row = [&](int r) { return g.keep_all ? g.c + s0 + r : sel[s0 + r]; };
-    auto src_tok = [&](int r) { return g.keep_all ? s0 + r : sel[g.T + s0 + r]; };
-    if (tid < rows) {
-      const int dst = dst_row(tid), t = src_tok(tid);
-      if (dst >= 0 && dst < g.B && t >= 0 && t < g.T)
-        g.pos_next[(int64_t)h * g.B + dst] = g.pos_offset + g.frame_base + t;
-    }
-    if (!g.kc_next) return;  // positions only
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int it = tid + i * kCopyThreads;
-      const int which = it / (kRowsPerBlock * CH);
-      const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
-      if (r < rows) {
-        const int t = min(max(src_tok(r), 0), g.T - 1);
-        buf[i] = *reinterpret_cast<const u32x4*>((which ? g.vf : g.kf) +
-                                                 ((int64_t)t * g.Hkv + h) * D + col);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int it = tid + i * kCopyThreads;
-      const int which = it / (kRowsPerBlock * CH);
-      const int r = (it / CH) % kRowsPerBlock, col = (it % CH) * 8;
-      if (r < rows) {
-        const int dst = dst_row(r);
-        if (dst >= 0 && dst < g.B)
-          *reinterpret_cast<u32x4*>((which ? g.vc_next : g.kc_next) + ((int64_t)h * g.B + dst) * D +
-                                    col) = buf[i];
-      }
-    }
-    return;
-  }
   if (b < gather_blocks) {
     const int per_h = (g.newc + kRowsPerBlock - 1) / kRowsPerBlock;
     const int h = b / per_h;
@@ -157,8 +113,7 @@ hipError_t launch(const GatherArgs& g, int D, int gather_blocks, int append_bloc
 }  // namespace
 
 hipError_t launch_gather_append(const GatherArgs& g, int D, const Stream& st) {
-  const int gather_rows = g.in_place ? g.T : g.newc;
-  const int gather_blocks = g.Hkv * ((gather_rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int gather_blocks = g.Hkv * ((g.newc + kRowsPerBlock - 1) / kRowsPerBlock);
   const int append_blocks = g.kd ? g.Hkv * ((g.T + kRowsPerBlock - 1) / kRowsPerBlock) : 0;
   return launch(g, D, gather_blocks, append_blocks, st);
 }

@@ -25,7 +25,10 @@
 // outright; the output is the list of rows to refill (evicted rows in row
 // order, then the unused rows while C fills) and the kept frame tokens in
 // frame order.  The recency window ranks the candidates by position the same
-// way.
+// way.  The selecting workgroup then copies those frame tokens into their
+// rows itself (at most T rows per head), and extra workgroups of the launch
+// append the frame to the detailed cache, so the in-place step needs no
+// separate state-update launch.
 #include "../skv_internal.h"
 
 namespace skv {
@@ -35,6 +38,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 static_assert(kMaxPool / kSelWaves < 65536, "16-bit per-wave histogram counters");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline uint32_t score_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -125,7 +129,55 @@ struct SelectJob {
   int ldsel;
   int recent;             // keep the last min(pool, budget) entries (most recent)
   InPlace ip;             // ip.pos null: the pool is in position order
+  int all_heads;          // the layer-wide job: its selection serves every head
 };
+
+// In place, the move lists live in LDS past the pool's keys when they fit.
+__host__ __device__ inline bool in_place_lds_fits(int pool, int T) {
+  return (int64_t)pool + 2 * (int64_t)T <= kMaxPool;
+}
+
+// In place: copies M moved frame tokens of heads [h0, h1) into their state
+// rows (K and V rows, 16-byte chunks, up to kMoveU loads in flight per
+// thread) and writes their positions.  Move r goes to row mv[r] and comes
+// from frame token mv[T + r]; mv null: rows c + r from token r (the frame is
+// appended while C fills).
+constexpr int kMoveU = 8;
+__device__ void apply_moves(const InPlace& ip, const int32_t* mv, int M, int h0, int h1) {
+  const int tid = threadIdx.x;
+  const int nh = h1 - h0;
+  auto dst_of = [&](int r) { return mv ? mv[r] : ip.c + r; };
+  auto src_of = [&](int r) { return mv ? mv[ip.T + r] : r; };
+  for (int i = tid; i < nh * M; i += kSelThreads) {
+    const int h = h0 + i / M, r = i % M;
+    ip.pos[(int64_t)h * ip.ldpos + dst_of(r)] = ip.frame_pos0 + src_of(r);
+  }
+  if (!ip.kc) return;  // the state is kept as positions into D
+  const int CH = ip.D / 8;
+  const int64_t items = (int64_t)nh * M * 2 * CH;  // (head, move, K/V, chunk), chunk fastest
+  for (int64_t base = 0; base < items; base += kMoveU * kSelThreads) {
+    u32x4 buf[kMoveU];
+    uint16_t* dst[kMoveU];
+#pragma unroll
+    for (int u = 0; u < kMoveU; ++u) {
+      const int64_t it = base + u * kSelThreads + tid;
+      dst[u] = nullptr;
+      if (it < items) {
+        const int ch = (int)(it % CH);
+        const int64_t rest = it / CH;
+        const int which = (int)(rest & 1);
+        const int64_t mr = rest >> 1;
+        const int h = h0 + (int)(mr / M), r = (int)(mr % M);
+        const int64_t src = ((int64_t)src_of(r) * ip.Hkv + h) * ip.D + ch * 8;
+        buf[u] = *reinterpret_cast<const u32x4*>((which ? ip.vf : ip.kf) + src);
+        dst[u] = (which ? ip.vc : ip.kc) + ((int64_t)h * ip.ldpos + dst_of(r)) * ip.D + ch * 8;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMoveU; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = buf[u];
+  }
+}
 
 struct SumJob {
   const f32x4* part;      // [S][n4]
@@ -145,6 +197,8 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   const int tid = threadIdx.x, w = tid >> 6;
   const int pool = J.pool, budget = J.budget;
   const float* sp = J.sig_part + (int64_t)h * J.rt * J.ldsig;
+  const bool in_place = J.sel && J.ip.pos != nullptr;
+  const bool lists_lds = in_place && in_place_lds_fits(pool, J.ip.T);
 
   // importance = sum of the row tiles' partial column sums, in tile order;
   // every load of a batch (kLoad candidates x kRows row tiles per thread) is
@@ -185,11 +239,14 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   }
   if (!J.sel) return;  // scores only (per-head rows of the SHARED mode)
   int32_t* out = J.sel + (int64_t)h * J.ldsel;
-  const bool in_place = J.ip.pos != nullptr;
+  // heads whose rows this job updates (the layer-wide job: every head)
+  const int mh0 = J.all_heads ? 0 : h, mh1 = J.all_heads ? J.ip.Hkv : h + 1;
   if (pool <= budget) {  // nothing is dropped
     if (!in_place)
       for (int j = tid; j < pool; j += kSelThreads) out[j] = j;
-    return;  // in place, the frame is simply appended
+    else
+      apply_moves(J.ip, nullptr, J.ip.T, mh0, mh1);  // the frame joins C at rows c..
+    return;
   }
   if (J.recent && !in_place) {  // the pool is in position order: the newest entries are last
     const int keepn = min(pool, budget);
@@ -343,27 +400,70 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   uint32_t tot;
   const uint32_t packed2 = block_exclusive_scan(nev | (nkf << 16), red, &tot);
   uint32_t e = packed2 & 0xFFFFu, f = packed2 >> 16;
+  // the lists: freed rows at [0, T), kept frame tokens at [T, 2T) -- in LDS
+  // past the keys when they fit, else in the selection row (global)
+  int32_t* lst = lists_lds ? reinterpret_cast<int32_t*>(keys) + pool : out;
   eqr = eq_before;
   for (int j = j0; j < j1; ++j) {
     const bool keep = kept(j, eqr);
     if (j < c) {
-      if (!keep) out[e++] = j;
+      if (!keep) lst[e++] = j;
     } else if (keep) {
-      out[T + f++] = j - c;
+      lst[T + f++] = j - c;
     }
   }
   const uint32_t evicted = tot & 0xFFFFu;
-  for (int r = tid; r < budget - c; r += kSelThreads) out[evicted + r] = c + r;
-  if (tid == 0) out[2 * T] = (int32_t)(tot >> 16);
+  for (int r = tid; r < budget - c; r += kSelThreads) lst[evicted + r] = c + r;
+  const int M = min((int)(tot >> 16), T);
+  if (tid == 0) out[2 * T] = M;
+  // the lists are read back by other threads of this workgroup: the barrier
+  // makes the writes above visible to them
+  __syncthreads();
+  apply_moves(J.ip, lst, M, mh0, mh1);
+}
+
+// Detailed-cache append over the append workgroups (grid-stride over
+// (token, head, K/V, chunk), chunk fastest).
+__device__ void append_frame(const AppendJob& A, int blk, int nblk) {
+  const int CH = A.D / 8;
+  const int64_t items = (int64_t)A.T * A.Hkv * 2 * CH;
+  const int64_t stride = (int64_t)nblk * kSelThreads;
+  for (int64_t base = (int64_t)blk * kSelThreads; base < items; base += kMoveU * stride) {
+    u32x4 buf[kMoveU];
+    uint16_t* dst[kMoveU];
+#pragma unroll
+    for (int u = 0; u < kMoveU; ++u) {
+      const int64_t it = base + u * stride + threadIdx.x;
+      dst[u] = nullptr;
+      if (it < items) {
+        const int ch = (int)(it % CH);
+        const int64_t rest = it / CH;
+        const int which = (int)(rest & 1);
+        const int64_t th = rest >> 1;
+        const int h = (int)(th % A.Hkv);
+        const int64_t t = th / A.Hkv;
+        buf[u] = *reinterpret_cast<const u32x4*>((which ? A.vf : A.kf) +
+                                                 (t * A.Hkv + h) * A.D + ch * 8);
+        int64_t slot = A.frame_base + t;
+        if (A.ring) slot %= A.cap;
+        dst[u] = (which ? A.vd : A.kd) + ((int64_t)h * A.cap + slot) * A.D + ch * 8;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMoveU; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = buf[u];
+  }
 }
 
 // Blocks [0, n_select) handle one KV head each (scores, and the selection
 // unless J.sel is null); block n_select, when n_shared is 1, selects once for
 // the whole layer from the scores summed over every KV head (J2: the
-// Hkv x rt partial rows read as one list, h-major); the remaining blocks sum
-// the split O partials (grid-stride over their share).
+// Hkv x rt partial rows read as one list, h-major); the next n_append blocks
+// append the frame to the detailed cache; the remaining blocks sum the split
+// O partials (grid-stride over their share).
 __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, int n_select,
                                                                  SelectJob J2, int n_shared,
+                                                                 AppendJob A, int n_append,
                                                                  SumJob Sj) {
   if ((int)blockIdx.x < n_select) {
     select_one_head(J, blockIdx.x);
@@ -374,6 +474,11 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
     return;
   }
   n_select += n_shared;
+  if ((int)blockIdx.x < n_select + n_append) {
+    append_frame(A, blockIdx.x - n_select, n_append);
+    return;
+  }
+  n_select += n_append;
   const int64_t nb = gridDim.x - n_select;
   for (int64_t i = (int64_t)(blockIdx.x - n_select) * kSelThreads + threadIdx.x; i < Sj.n4;
        i += nb * kSelThreads) {
@@ -385,7 +490,8 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
 
 namespace {
 hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& J2, int n_shared,
-                             const SumJob& Sj, int sum_blocks, const Stream& st) {
+                             const AppendJob& A, int n_append, const SumJob& Sj, int sum_blocks,
+                             const Stream& st) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_sum_kernel),
@@ -394,10 +500,13 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const size_t lds = (size_t)J.pool * sizeof(uint32_t);
-  hipExtLaunchKernelGGL(select_sum_kernel, dim3(n_select + n_shared + sum_blocks),
+  size_t words = (size_t)J.pool;
+  if ((J.ip.pos || J2.ip.pos) && in_place_lds_fits(J.pool, J.ip.T))
+    words = (size_t)J.pool + 2 * (size_t)J.ip.T;
+  const size_t lds = words * sizeof(uint32_t);
+  hipExtLaunchKernelGGL(select_sum_kernel, dim3(n_select + n_shared + n_append + sum_blocks),
                         dim3(kSelThreads), lds, st.st, st.start, st.stop, 0, J, n_select, J2,
-                        n_shared, Sj);
+                        n_shared, A, n_append, Sj);
   return hipGetLastError();
 }
 }  // namespace
@@ -405,12 +514,13 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& 
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o, bool shared,
-                         bool recent, const InPlace& ip, const Stream& st) {
+                         bool recent, const InPlace& ip, const AppendJob* app,
+                         const Stream& st) {
   shared = shared && !recent;  // the recency window is the same for every head
   SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, shared ? nullptr : sel,
-                 ldsel, recent ? 1 : 0, ip};
+                 ldsel, recent ? 1 : 0, ip, 0};
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
-  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip};
+  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};
   int sum_blocks = 0;
@@ -418,7 +528,15 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
     const int64_t want = (Sj.n4 + kSelThreads - 1) / kSelThreads;
     sum_blocks = (int)(want < 1024 ? want : 1024);
   }
-  return launch_select_sum(J, hkv, J2, shared ? 1 : 0, Sj, sum_blocks, st);
+  AppendJob A = {};
+  int n_append = 0;
+  if (app) {
+    A = *app;
+    const int64_t items = (int64_t)A.T * A.Hkv * 2 * (A.D / 8);
+    const int64_t want = (items + kSelThreads - 1) / kSelThreads;
+    n_append = (int)(want < 256 ? want : 256);
+  }
+  return launch_select_sum(J, hkv, J2, shared ? 1 : 0, A, n_append, Sj, sum_blocks, st);
 }
 
 }  // namespace skv

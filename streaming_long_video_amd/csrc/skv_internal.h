@@ -47,11 +47,29 @@ struct AttnArgs {
 hipError_t launch_attn_stats(const AttnArgs& a, int D, const Stream& st);
 // In-place (slot-stable) state update: positions of the state rows ([Hkv][ldpos]),
 // live rows c, frame tokens T and the frame's first position.  pos null: the
-// pool is in position order and the selection lists kept pool indices.
+// pool is in position order and the selection lists kept pool indices.  The
+// selecting workgroup also moves the kept frame tokens (kf, vf: [T][Hkv][D])
+// into their rows of kc, vc ([Hkv][ldpos][D]; null: positions only) and
+// writes their positions.
 struct InPlace {
-  const int64_t* pos;
+  int64_t* pos;
   int ldpos, c, T;
   int64_t frame_pos0;
+  const uint16_t* kf;
+  const uint16_t* vf;
+  uint16_t* kc;
+  uint16_t* vc;
+  int Hkv, D;
+};
+// Detailed-cache append done by extra workgroups of the select launch:
+// D[h][slot(frame_base + t)] = frame token t.
+struct AppendJob {
+  const uint16_t* kf;  // [T][Hkv][D]
+  const uint16_t* vf;
+  uint16_t* kd;        // [Hkv][cap][D]
+  uint16_t* vd;
+  int64_t cap, frame_base;
+  int T, Hkv, D, ring;
 };
 hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
 // One launch: per KV head, sums the score partials (scores may be null),
@@ -59,11 +77,13 @@ hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
 // and S > 1, o[i] = sum_{s<S} o_part[s*o_elems + i] in split order.
 // Standalone mode: rt = 1 and sig_part holds the scores.  In place (ip.pos
 // set), each selection row holds the rows to refill at [0, T), the kept frame
-// tokens at [T, 2T) and their count at 2T.
+// tokens at [T, 2T) and their count at 2T, and the launch applies the moves;
+// app (may be null) adds the detailed-cache append to the same launch.
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
                          int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
                          const float* o_part, int S, int64_t o_elems, float* o, bool shared,
-                         bool recent, const InPlace& ip, const Stream& st);
+                         bool recent, const InPlace& ip, const AppendJob* app,
+                         const Stream& st);
 
 struct GatherArgs {
   const uint16_t* kc_prev;  // [Hkv][B][D]
@@ -72,7 +92,7 @@ struct GatherArgs {
   const uint16_t* kf;       // [T][Hkv][D]
   const uint16_t* vf;
   const int32_t* sel;       // [Hkv][sel_stride] pool indices, ascending (ignored if
-                            // keep_all), or the move lists of the in-place update
+                            // keep_all)
   int sel_stride;           // selection row stride, or 0 when one kept set serves
                             // every head (SHARED)
   uint16_t* kc_next;        // null: positions only (state kept as positions into D)
@@ -86,8 +106,6 @@ struct GatherArgs {
   int B, T, Hkv, c, newc;
   int keep_all;             // pool <= B: C_n = [C_{n-1} ; frame]
   int ring;
-  int in_place;             // C_{n-1} is updated in place (kc_next == kc_prev):
-                            // only the kept frame tokens move, into freed rows
 };
 hipError_t launch_gather_append(const GatherArgs& g, int D, const Stream& st);
 hipError_t launch_append_only(const GatherArgs& g, int D, const Stream& st);

@@ -189,13 +189,32 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
               [&](const skv::Stream& ks) { return skv::launch_attn_stats(a1, p.D, ks); });
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_ATTN_OUT, st, [&](const skv::Stream& ks) { return skv::launch_attn_out(a, p.D, ks); });
+  // in place, the select launch also moves the kept frame tokens into C and
+  // appends the frame to D: no state-update launch follows
   skv::InPlace ip = {};
+  skv::AppendJob app = {};
   if (in_place) {
     ip.pos = at<int64_t>(L, p.off_cpos[cur]);
     ip.ldpos = p.B;
     ip.c = c;
     ip.T = p.T;
     ip.frame_pos0 = p.offset + L->n * (int64_t)p.T;
+    ip.kf = a.kf;
+    ip.vf = a.vf;
+    ip.kc = c_in_d ? nullptr : at<uint16_t>(L, p.off_ck[cur]);
+    ip.vc = c_in_d ? nullptr : at<uint16_t>(L, p.off_cv[cur]);
+    ip.Hkv = p.Hkv;
+    ip.D = p.D;
+    app.kf = a.kf;
+    app.vf = a.vf;
+    app.kd = at<uint16_t>(L, p.off_dk);
+    app.vd = at<uint16_t>(L, p.off_dv);
+    app.cap = p.cap;
+    app.frame_base = L->n * (int64_t)p.T;
+    app.T = p.T;
+    app.Hkv = p.Hkv;
+    app.D = p.D;
+    app.ring = ring;
   }
   if (e == hipSuccess)
     e = timed(L, STATEKV_KERNEL_SELECT, st, [&](const skv::Stream& ks) {
@@ -203,9 +222,10 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
                                 p.ldsel, a.S > 1 ? opart : nullptr, a.S,
                                 (int64_t)p.T * p.Hq * p.D, o, shared,
-                                (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ip, ks);
+                                (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ip,
+                                in_place ? &app : nullptr, ks);
     });
-  if (e == hipSuccess) {
+  if (e == hipSuccess && !in_place) {
     skv::GatherArgs g = {};
     g.kc_prev = c_in_d ? nullptr : a.kc;
     g.vc_prev = c_in_d ? nullptr : a.vc;
@@ -229,7 +249,6 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
     g.newc = newc;
     g.keep_all = pool <= p.B;
     g.ring = ring;
-    g.in_place = in_place;
     e = timed(L, STATEKV_KERNEL_GATHER, st,
               [&](const skv::Stream& ks) { return skv::launch_gather_append(g, p.D, ks); });
   }
@@ -501,7 +520,7 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
                                        budget, nullptr, 1, 0, nullptr, false, false,
-                                       skv::InPlace{}, st));
+                                       skv::InPlace{}, nullptr, st));
 }
 
 }  // extern "C"

@@ -291,10 +291,28 @@ def test_in_place_ties_go_to_lower_positions():
     (12, 2, 128, 256, 2048, 12),
     (8, 4, 64, 33, 1, 4),
 ])
-def test_ragged_and_edge_shapes(shape):
+@pytest.mark.parametrize("in_place", [False, True])
+def test_ragged_and_edge_shapes(shape, in_place):
     Hq, Hkv, d, T, B, N = shape
     spec = framegen.FrameSpec(Hq, Hkv, d, T, N, B, 1e4, 11, sinks=False)
-    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec)
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SLOT_STABLE if in_place else 0)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec, layer=layer)
+    _assert_reports(reports, exact_select=False)
+    check_caches_bitwise(layer, ks, vs)
+
+
+@pytest.mark.parametrize("d,shared", [(64, False), (128, True)])
+def test_in_place_large_frame(d, shared):
+    """T = 4096 (the largest frame): the in-place move lists no longer fit in
+    LDS beside the pool's keys (B = 24000) and go through the selection rows;
+    with d = 128 and SHARED the moves of every head are copied by one
+    workgroup.  Seven frames, the last two evicting; teacher-forced."""
+    Hkv = 2 if shared else 1
+    spec = framegen.FrameSpec(Hkv, Hkv, d, 4096, 7, 24000, 1e4, 17, sinks=False)
+    f = skv.STATEKV_FLAG_SLOT_STABLE | (skv.STATEKV_FLAG_SELECT_SHARED if shared else 0)
+    layer = _layer(spec, flags=f)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec, layer=layer,
+                                                       orc_kw=dict(shared=shared))
     _assert_reports(reports, exact_select=False)
     check_caches_bitwise(layer, ks, vs)
 
