@@ -59,7 +59,18 @@ constexpr int kThreads = kWaves * 64;
 // boundaries of the block step (operand reads / softmax / MFMA issue).
 #define SKV_FENCE() __builtin_amdgcn_sched_barrier(0)
 constexpr int kKPad = 8;  // bf16 padding per K row in LDS (conflict-free b128 reads)
-constexpr int kVPad = 4;  // fp16 padding per V^T row (conflict-free b64 reads)
+constexpr int kVPad = 8;  // fp16 padding per V^T row (conflict-free b128 reads)
+constexpr int kScoreTiles = 64;  // key tiles of scores buffered in LDS per flush
+// s_waitcnt operand for vmcnt(0) with the other counters left alone
+// (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Position of key k of a tile within a V^T row in LDS: in every 16-key slab
+// the key groups 4-7 and 8-11 trade places, so that the 8 keys one lane feeds
+// to the PV MFMA (slots 8(r/4) + 4 half + r%4, r < 8) are contiguous.
+__host__ __device__ constexpr int vt_pos(int k) {
+  return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
 constexpr float kPUnscale = 1.f / 4096.f;  // P is formed as 2^12 * P
 
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each
@@ -126,21 +137,24 @@ __device__ inline uint32_t pack_f16(float a, float b) {
 
 // Row of the state buffer that holds state token j of KV head h: j itself, or
 // (with the state kept as positions into D) the D row of its position.
+template <bool CIND>
 __device__ inline int64_t state_row(const AttnArgs& a, int h, int j) {
-  return a.cpos ? a.cpos[(int64_t)h * a.ldcp + j] - a.cpos_base : (int64_t)j;
+  if constexpr (CIND) return a.cpos[(int64_t)h * a.ldcp + j] - a.cpos_base;
+  return (int64_t)j;
 }
 
-// One 16-byte chunk (8 bf16) of pool row j, columns [col, col+8); zero past the pool.
-template <int D>
+// One 16-byte chunk (8 bf16) of pool row j, columns [col, col+8).  Rows past
+// the pool read the last pool row instead: every such key is masked (its
+// weight is exactly 0), and a finite stand-in keeps 0 * value at 0.  One load
+// from a selected address, so the staged registers have a single source.
+template <int D, bool CIND>
 __device__ inline u32x4 pool_chunk(const AttnArgs& a, const uint16_t* state,
                                    const uint16_t* frame, int h, int pool, int j, int col) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (j < a.c)
-    v = *reinterpret_cast<const u32x4*>(state + ((int64_t)h * a.ldc + state_row(a, h, j)) * D +
-                                        col);
-  else if (j < pool)
-    v = *reinterpret_cast<const u32x4*>(frame + ((int64_t)(j - a.c) * a.Hkv + h) * D + col);
-  return v;
+  const int jj = min(j, pool - 1);
+  const uint16_t* p =
+      jj < a.c ? state + ((int64_t)h * a.ldc + state_row<CIND>(a, h, jj)) * D + col
+               : frame + ((int64_t)(jj - a.c) * a.Hkv + h) * D + col;
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Registers staging one key tile between its global loads and its LDS stores.
@@ -156,11 +170,12 @@ struct TileStage {
   u32x4 k[KCH];
   u32x4 v0[WITH_V ? VIT : 1], v1[WITH_V ? VIT : 1];
 
+  template <bool CIND>
   __device__ inline void load(const AttnArgs& a, int h, int pool, int key0, int tid) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ch = tid + i * kThreads;
-      k[i] = pool_chunk<D>(a, a.kc, a.kf, h, pool, key0 + ch / (D / 8), (ch % (D / 8)) * 8);
+      k[i] = pool_chunk<D, CIND>(a, a.kc, a.kf, h, pool, key0 + ch / (D / 8), (ch % (D / 8)) * 8);
     }
     if constexpr (WITH_V) {
 #pragma unroll
@@ -168,8 +183,8 @@ struct TileStage {
         const int it = tid + i * kThreads;
         if (VPART && it >= VITEMS) continue;
         const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
-        v0[i] = pool_chunk<D>(a, a.vc, a.vf, h, pool, key0 + 2 * kp, dc);
-        v1[i] = pool_chunk<D>(a, a.vc, a.vf, h, pool, key0 + 2 * kp + 1, dc);
+        v0[i] = pool_chunk<D, CIND>(a, a.vc, a.vf, h, pool, key0 + 2 * kp, dc);
+        v1[i] = pool_chunk<D, CIND>(a, a.vc, a.vf, h, pool, key0 + 2 * kp + 1, dc);
       }
     }
   }
@@ -232,7 +247,7 @@ struct TileStage {
         const int it = tid + i * kThreads;
         if (VPART && it >= VITEMS) continue;
         const int kp = it % (kKeyTile / 2), dc = (it / (kKeyTile / 2)) * 8;
-        uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[dc * VLD + 2 * kp]);
+        uint32_t* col = reinterpret_cast<uint32_t*>(&Vt[dc * VLD + vt_pos(2 * kp)]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           col[(2 * e) * (VLD / 2)] = pack_f16(bf16lo(v0[i][e]), bf16lo(v1[i][e]));
@@ -254,15 +269,15 @@ struct StateRows {
   __device__ inline void load(const AttnArgs& a, int h, int key0, int tid) {
 #pragma unroll
     for (int i = 0; i < TS::KCH; ++i)
-      k[i] = (int32_t)state_row(a, h, key0 + (tid + i * kThreads) / (D / 8));
+      k[i] = (int32_t)state_row<true>(a, h, key0 + (tid + i * kThreads) / (D / 8));
     if constexpr (WITH_V) {
 #pragma unroll
       for (int i = 0; i < TS::VIT; ++i) {
         const int it = tid + i * kThreads;
         if (TS::VPART && it >= TS::VITEMS) continue;
         const int kp = it % (kKeyTile / 2);
-        v0[i] = (int32_t)state_row(a, h, key0 + 2 * kp);
-        v1[i] = (int32_t)state_row(a, h, key0 + 2 * kp + 1);
+        v0[i] = (int32_t)state_row<true>(a, h, key0 + 2 * kp);
+        v1[i] = (int32_t)state_row<true>(a, h, key0 + 2 * kp + 1);
       }
     }
   }
@@ -280,10 +295,15 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
   constexpr int KLD = D + kKPad;
   constexpr int VLD = KT + kVPad;
+  static_assert(VLD % 8 == 0, "16-byte aligned V^T rows");
   constexpr bool WITH_V = PASS >= 2;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KLD];
   __shared__ __attribute__((aligned(16))) _Float16 Vt[WITH_V ? 2 : 1][WITH_V ? D * VLD : 8];
   __shared__ float sigw[PASS == 2 ? 2 : 1][PASS == 2 ? kWaves * KT : 1];
+  // the row tile's finished scores of up to kScoreTiles key tiles, stored to
+  // global memory in bursts (a store inside the tile loop would make the next
+  // tile's loads wait for it)
+  __shared__ float sbuf[PASS == 2 ? kScoreTiles * KT : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -338,7 +358,7 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
         stage.load_state(a, h, key0, tid);
       }
     } else {
-      stage.load(a, h, pool, key0, tid);
+      stage.template load<CIND>(a, h, pool, key0, tid);
     }
   };
   if (CIND && (tile_lo + 1) * KT <= c) rows.load(a, h, tile_lo * KT, tid);
@@ -450,17 +470,15 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
         sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qreg[i][kk], sacc[i], 0, 0, 0);
   };
   // V^T rows (d) of block kb as the A operand of O^T = V^T P^T, key slots in
-  // the order of the logits' registers (8(r/4) + 4 half + r%4)
+  // the order of the logits' registers (8(r/4) + 4 half + r%4): one 16-byte
+  // read, the rows being stored in vt_pos order
   auto read_v = [&](const _Float16* V, int kb, u32x4 (&vf)[NMB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int slab = 0; slab < 2; ++slab) {
-        const _Float16* vrow = &V[(mb * 32 + l32) * VLD + kb * 32 + slab * 16 + 4 * half];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        vf[mb][slab] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
+      for (int slab = 0; slab < 2; ++slab)
+        vf[mb][slab] = *reinterpret_cast<const u32x4*>(
+            &V[(mb * 32 + l32) * VLD + kb * 32 + slab * 16 + 8 * half]);
   };
   auto mfma_pv = [&](const u32x4 (&vf)[NMB][2], const u32x4 (&ph)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -571,15 +589,26 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
     }
   };
 
+  // Thread tid < KT owns key tid of every tile: it sums the waves' column sums
+  // of a finished tile into sbuf and later stores its own entries, so no
+  // barrier orders the two.
   auto emit_scores = [&](int tile, const float* sw) __attribute__((always_inline)) {
     if constexpr (PASS == 2) {
       if (tid < KT) {
-        const int j = tile * KT + tid;
-        if (j < pool) {
-          float acc = 0.f;
+        float acc = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) acc += sw[ww * KT + tid];
-          a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = acc;
+        for (int ww = 0; ww < kWaves; ++ww) acc += sw[ww * KT + tid];
+        sbuf[((tile - tile_lo) % kScoreTiles) * KT + tid] = acc;
+      }
+    }
+  };
+  auto flush_scores = [&](int t0, int t1) __attribute__((always_inline)) {  // tiles [t0, t1]
+    if constexpr (PASS == 2) {
+      if (tid < KT) {
+        float* dst = a.sig_part + ((int64_t)h * a.rt + rtile) * a.ldsig;
+        for (int t = t0; t <= t1; ++t) {
+          const int j = t * KT + tid;
+          if (j < pool) dst[j] = sbuf[((t - tile_lo) % kScoreTiles) * KT + tid];
         }
       }
     }
@@ -590,14 +619,20 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
     stage.store(Ks[0], Vt[0], tid);
     __syncthreads();
   }
+  // nothing loaded before the loop is still in flight: otherwise the wait for
+  // it (on a path the compiler cannot rule out) would sit inside the loop and
+  // hold up every tile's prefetch
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   for (int tile = tile_lo; tile < tile_end; ++tile) {
     const int cur = (tile - tile_lo) & 1;
     const int key0 = tile * KT;
     const bool more = tile + 1 < tile_end;
-    if (more) stage_load(key0 + KT);
+    // the previous tile's score store goes out before the next tile's loads,
+    // so that no wait for the store holds the loads up
     if constexpr (PASS == 2) {
       if (tile > tile_lo) emit_scores(tile - 1, sigw[cur ^ 1]);
     }
+    if (more) stage_load(key0 + KT);
     bf16x8 kf[NKK];
     read_k(Ks[cur], 0, kf);
 #pragma unroll
@@ -631,12 +666,24 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
         SKV_FENCE();
       }
     }
+    if constexpr (PASS == 2) {
+      // the buffer is full: store it, and wait here (rarely) rather than
+      // leave stores in flight into the next tile
+      if (tile > tile_lo && (tile - 1 - tile_lo) % kScoreTiles == kScoreTiles - 1) {
+        flush_scores(tile - kScoreTiles, tile - 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      }
+    }
     if (more) stage.store(Ks[cur ^ 1], Vt[WITH_V ? cur ^ 1 : 0], tid);
     __syncthreads();
   }
 
   if constexpr (PASS == 2) {
-    if (tile_end > tile_lo) emit_scores(tile_end - 1, sigw[(tile_end - 1 - tile_lo) & 1]);
+    if (tile_end > tile_lo) {
+      emit_scores(tile_end - 1, sigw[(tile_end - 1 - tile_lo) & 1]);
+      const int t1 = tile_end - 1;
+      flush_scores(max(tile_lo, t1 - (t1 - tile_lo) % kScoreTiles), t1);
+    }
     // key tiles of this split that no query of the row tile can see
     for (int j = tile_end * KT + tid; j < min(tile_hi * KT, pool); j += kThreads)
       a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = 0.f;
