@@ -7,6 +7,7 @@ and the benchmark's CPU-baseline leg may import it; the GPU library never does.
 from .statekv_oracle import (  # noqa: F401
     FrameResult,
     StateKVOracle,
+    attention_mass_diagnostics,
     decode_attention,
     decode_bf16,
     frame_attention,

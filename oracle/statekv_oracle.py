@@ -377,6 +377,51 @@ def rope_at_positions(x, positions, theta: float, scaling: float = 1.0) -> np.nd
     return np.concatenate([z.real, z.imag], axis=-1)
 
 
+def attention_mass_diagnostics(scores, n_history: int, budget: int, prev_kept=None):
+    """The App. A measurements of one frame (paperlayer summary, App. A.1-A.3).
+
+    ``scores``: importance of every token seen through this frame, in
+    ascending position, aggregated over the layer's query heads and the
+    frame's queries under attention over every available token (App. A
+    "Protocol"); the first ``n_history`` tokens belong to earlier frames.
+    ``prev_kept``: boolean mask over those earlier tokens, the set this
+    function returned for the previous frame (None before it).
+
+    Returns (topb_mass, recency_mass, recall, kept):
+
+    * topb_mass (A.1, concentration): the share of the historical attention
+      mass held by the ``budget`` largest historical importances;
+    * recency_mass (A.3, recency retention): the share held by the ``budget``
+      most recent historical tokens;
+    * kept (A.2, the oracle state): the top-``budget`` of all tokens through
+      this frame, ties to the lower position, as a boolean mask;
+    * recall (A.2, weighted candidate-pool recall): the share of the kept
+      set's importance that lies in the candidate pool, i.e. the previous
+      frame's kept set plus this frame's tokens.
+
+    NaN where a share has no mass to divide (no earlier frame).
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    L, c = scores.shape[0], int(n_history)
+    b = int(budget)
+    hist = scores[:c]
+    total = hist.sum()
+    bb = min(b, c)
+    if c == 0 or total <= 0.0:
+        topb = recency = math.nan
+    else:
+        topb = np.sort(hist)[::-1][:bb].sum() / total
+        recency = hist[c - bb:].sum() / total
+    kept = np.zeros(L, dtype=bool)
+    kept[select_top_b(scores, np.arange(L), b)] = True
+    pool = np.ones(L, dtype=bool)
+    if prev_kept is not None:
+        pool[:c] = np.asarray(prev_kept, dtype=bool)[:c]
+    kept_mass = scores[kept].sum()
+    recall = scores[kept & pool].sum() / kept_mass if kept_mass > 0.0 else math.nan
+    return float(topb), float(recency), float(recall), kept
+
+
 def round_to_bf16(x) -> np.ndarray:
     """float64 -> nearest bfloat16 (8 significant bits, ties to even), as
     uint16 bit patterns.  Normal range only (finite values whose magnitude is

@@ -8,6 +8,7 @@ force.  The same checks run against deliberately broken copies of the oracle
 
 from __future__ import annotations
 
+import itertools
 import json
 import math
 import os
@@ -280,6 +281,48 @@ def check_recency_window() -> None:
         hi = (n + 1) * T
         assert list(r.kept_positions[0]) == list(range(max(0, hi - B), hi)), (n, r.kept_positions)
 
+def check_attention_mass() -> None:
+    """App. A diagnostics: a case worked by hand; closed forms (uniform
+    importance gives min(b, c)/c for both shares, ties kept at the lower
+    positions); the top-b share is the best share over every subset of b
+    historical tokens (brute force); the recency share is that of the b most
+    recent ones; the recall is 1 when the kept set stays in the pool and 0
+    when the pool misses the only kept token."""
+    # by hand: history [5, 1, 3, 0.5], frame [2, 4], b = 2: top-2 history
+    # 5 + 3 of 9.5; the last two 3 + 0.5; the new set {5, 4}; the pool holds
+    # positions 1, 2 and the frame, so only 4 of the 9 is recalled
+    t, r, rc, kept = so.attention_mass_diagnostics([5, 1, 3, 0.5, 2, 4], 4, 2,
+                                                   [False, True, True, False])
+    assert abs(t - 8 / 9.5) < 1e-15 and abs(r - 3.5 / 9.5) < 1e-15, (t, r)
+    assert kept.tolist() == [True, False, False, False, False, True], kept
+    assert abs(rc - 4 / 9) < 1e-15, rc
+    # no earlier frame: the shares are undefined, the pool is everything
+    t, r, rc, kept = so.attention_mass_diagnostics([1.0, 2.0], 0, 1)
+    assert math.isnan(t) and math.isnan(r) and rc == 1.0 and kept.tolist() == [False, True]
+    # uniform importance
+    for b in (1, 3, 7, 12):
+        t, r, _, kept = so.attention_mass_diagnostics(np.ones(12), 9, b)
+        assert abs(t - min(b, 9) / 9) < 1e-15 and abs(r - min(b, 9) / 9) < 1e-15, (b, t, r)
+        assert kept.tolist() == [i < b for i in range(12)], kept
+    # stable set -> recall 1; pool missing the single kept token -> 0
+    s = np.array([9.0, 1, 1, 1, 0.5, 0.5])
+    assert so.attention_mass_diagnostics(s, 4, 1, [True, False, False, False])[2] == 1.0
+    assert so.attention_mass_diagnostics(s, 4, 1, [False, True, True, True])[2] == 0.0
+    # brute force on small random histories
+    rng = np.random.default_rng(11)
+    for _ in range(30):
+        c, T, b = int(rng.integers(1, 8)), int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        s = rng.exponential(size=c + T)
+        t, r, _, kept = so.attention_mass_diagnostics(s, c, b, rng.random(c) < 0.5)
+        hist = s[:c]
+        best = max(sum(hist[list(S)]) for S in itertools.combinations(range(c), min(b, c)))
+        assert abs(t - best / hist.sum()) < 1e-12, (t, best)
+        assert abs(r - sum(hist[i] for i in range(c) if i >= c - b) / hist.sum()) < 1e-12
+        inside, outside = s[kept], s[~kept]
+        assert len(inside) == min(b, c + T)
+        assert not len(outside) or inside.min() >= outside.max()
+
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -291,4 +334,5 @@ ALL_CHECKS = [
     check_decode_attention,
     check_rope_and_rounding,
     check_recency_window,
+    check_attention_mass,
 ]

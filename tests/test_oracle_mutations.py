@@ -220,3 +220,51 @@ def test_recency_pin_catches_mutant(monkeypatch, mutant):
     monkeypatch.setattr(so, "select_most_recent", mutant)
     with pytest.raises(AssertionError):
         oracle_pins.check_recency_window()
+
+
+_orig_mass = so.attention_mass_diagnostics
+
+
+def mass_recency_takes_oldest(scores, n_history, budget, prev_kept=None):
+    t, _, rc, kept = _orig_mass(scores, n_history, budget, prev_kept)
+    h = np.asarray(scores, dtype=np.float64)[:n_history]
+    r = h[: min(budget, n_history)].sum() / h.sum() if n_history else float("nan")
+    return t, r, rc, kept
+
+
+def mass_history_includes_frame(scores, n_history, budget, prev_kept=None):
+    L = len(scores)
+    t, r, _, _ = _orig_mass(scores, L, budget, None)
+    _, _, rc, kept = _orig_mass(scores, n_history, budget, prev_kept)
+    return t, r, rc, kept
+
+
+def mass_recall_unweighted(scores, n_history, budget, prev_kept=None):
+    t, r, _, kept = _orig_mass(scores, n_history, budget, prev_kept)
+    pool = np.ones(len(kept), dtype=bool)
+    if prev_kept is not None:
+        pool[:n_history] = np.asarray(prev_kept, dtype=bool)[:n_history]
+    return t, r, float((kept & pool).sum() / kept.sum()), kept
+
+
+def mass_pool_without_frame(scores, n_history, budget, prev_kept=None):
+    t, r, _, kept = _orig_mass(scores, n_history, budget, prev_kept)
+    s = np.asarray(scores, dtype=np.float64)
+    pool = np.zeros(len(kept), dtype=bool)
+    pool[:n_history] = True if prev_kept is None else np.asarray(prev_kept, dtype=bool)
+    return t, r, float(s[kept & pool].sum() / s[kept].sum()), kept
+
+
+def mass_keeps_smallest(scores, n_history, budget, prev_kept=None):
+    s = -np.asarray(scores, dtype=np.float64)
+    t, r, rc, kept = _orig_mass(s, n_history, budget, prev_kept)
+    return t, r, rc, kept
+
+
+@pytest.mark.parametrize("mutant", [mass_recency_takes_oldest, mass_history_includes_frame,
+                                    mass_recall_unweighted, mass_pool_without_frame,
+                                    mass_keeps_smallest], ids=lambda f: f.__name__)
+def test_attention_mass_pin_catches_mutant(monkeypatch, mutant):
+    monkeypatch.setattr(so, "attention_mass_diagnostics", mutant)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_attention_mass()
