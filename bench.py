@@ -408,6 +408,51 @@ def run_decode(args):
 
 
 # ----------------------------------------------------------------------------
+# App. A diagnostics on the synthetic stream
+# ----------------------------------------------------------------------------
+
+MASS_BUDGETS = [1, 4, 16, 64, 256, 1024, 4096]
+
+
+def run_mass(args):
+    """A layer of the workload's shape that keeps every token (budget = the
+    whole history) over --mass-frames frames; after each frame the App. A
+    diagnostics: top-b historical mass share (A.1), recency share (A.3) and
+    weighted candidate-pool recall (A.2), averaged over frames 1.. ."""
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload(args.workload)
+    T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+    N = args.mass_frames
+    spec = spec.replace(n_frames=N, state_budget=N * T)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    layer = skv.Layer(Hq, Hkv, d, T, N * T, detailed_capacity=N * T)
+    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=min(16, os.cpu_count() or 1))
+    up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    q_d, k_d, v_d = up(qs), up(ks), up(vs)
+    sets, rows = None, []
+    for n in range(N):
+        layer.prefill(q_d[n], k_d[n], v_d[n])
+        out, sets = layer.attention_mass(MASS_BUDGETS, sets)
+        if n >= 1:
+            rows.append(out.cpu().numpy().astype(np.float64))
+    a = np.stack(rows)  # [frames][budget][3]
+    res = {}
+    for i, b in enumerate(MASS_BUDGETS):
+        res[str(b)] = {"topb_mass": float(np.nanmean(a[:, i, 0])),
+                       "recency_mass": float(np.nanmean(a[:, i, 1])),
+                       "pool_recall": float(np.nanmean(a[:, i, 2]))}
+    print(json.dumps({"mode": "mass", "workload": args.workload, "frames": N,
+                      "data": "synthetic (seeded N(0,1) bf16 Q/K/V, RoPE at original positions, "
+                              "planted temporal-sink keys in frames 0-3)",
+                      "averaged_over_frames": f"1..{N - 1}", "budgets": res}), flush=True)
+
+
+# ----------------------------------------------------------------------------
 # 28 layers of the 2B shape, layer-major per frame
 # ----------------------------------------------------------------------------
 
@@ -453,7 +498,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=496)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode"],
+    ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode", "mass"],
                     default="headline")
     ap.add_argument("--decode-queries", type=int, nargs="+", default=[1, 4],
                     help="text tokens per decoding call (decode mode)")
@@ -470,6 +515,8 @@ def main(argv=None):
                     default="rows",
                     help="C as its own K/V rows rewritten on update (rows), as positions into "
                          "D (positions), updated in place (inplace), or both")
+    ap.add_argument("--mass-frames", type=int, default=64,
+                    help="frames of the App. A diagnostics run (--mode mass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)
@@ -478,7 +525,7 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28,
-     "decode": run_decode}[args.mode](args)
+     "decode": run_decode, "mass": run_mass}[args.mode](args)
 
 
 if __name__ == "__main__":

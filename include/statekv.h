@@ -236,6 +236,30 @@ int statekv_reset_layer(statekv_layer* layer);
  * checkpoint (last_pool becomes 0). */
 int statekv_restore_layer(statekv_layer* layer, int64_t frames_seen, int32_t count);
 
+/* The App. A measurements of the last frame (paperlayer App. A.1-A.3), for a
+ * layer that has kept every token so far (state_budget >= frames_seen * T;
+ * STATEKV_ERR_INVALID_ARGUMENT otherwise, or before the first frame).  Such a
+ * layer computes full attention, and the importance its last
+ * statekv_prefill_frame left in the state view, summed over the KV heads, is
+ * the pages' aggregate over the layer's heads and the frame's queries.  For
+ * each budget b = budgets[i] (host array of n_budgets <= 64 values >= 1):
+ *   out[3i]     share of the historical mass (tokens of earlier frames) held
+ *               by the b largest historical importances (A.1);
+ *   out[3i + 1] share held by the b most recent historical tokens (A.3);
+ *   out[3i + 2] weighted candidate-pool recall (A.2): S_n = the b tokens
+ *               through this frame with the largest importance (ties to the
+ *               lower position); the share of S_n's importance inside S_{n-1}
+ *               plus this frame's tokens.
+ * out: device, 3 * n_budgets floats, NaN where a share is undefined (no
+ * earlier frame).  sets: device, n_budgets * statekv_mass_set_words() words,
+ * owned by the caller and kept between calls: S_{n-1} is read from it (when
+ * frames_seen > 1) and S_n written to it (bit j of word j/32 set when token
+ * j, counted from the first frame, is in the set).  Asynchronous on stream. */
+int statekv_attention_mass(statekv_layer* layer, const int32_t* budgets,
+                           int32_t n_budgets, uint32_t* sets, float* out, void* stream);
+/* Words per budget of the sets buffer of statekv_attention_mass (host only). */
+int statekv_mass_set_words(const statekv_layer* layer, int32_t* words);
+
 /* Release the host handle (the workspace stays the caller's). */
 int statekv_free_layer(statekv_layer* layer);
 
@@ -256,7 +280,8 @@ enum {
                                     launched with SLOT_STABLE)                  */
   STATEKV_KERNEL_DECODE = 5,     /* decoding over D: split partials            */
   STATEKV_KERNEL_ROPE = 6,       /* in-library rotary embedding of the frame   */
-  STATEKV_NUM_KERNELS = 7
+  STATEKV_KERNEL_MASS = 7,       /* App. A diagnostics                         */
+  STATEKV_NUM_KERNELS = 8
 };
 
 /* Timing hooks for benchmarks (measurement only; results are unaffected).

@@ -17,11 +17,13 @@ from ._binding import (  # noqa: F401
     StateKVError,
     load_library,
     make_config,
+    statekv_attention_mass,
     statekv_decode_attention,
     statekv_detailed_cache,
     statekv_free_layer,
     statekv_full_attention_frame,
     statekv_init_layer,
+    statekv_mass_set_words,
     statekv_prefill_frame,
     statekv_profile_start,
     statekv_profile_stop,

@@ -21,7 +21,7 @@ STATEKV_ERR_CAPACITY = -4
 STATEKV_ERR_HIP = -5
 
 STATEKV_KERNELS = ("attn_stats", "attn_out", "split_sum", "select", "gather", "decode",
-                   "rope")
+                   "rope", "mass")
 
 STATEKV_FLAG_SELECT_SHARED = 1 << 0
 STATEKV_FLAG_D_RING = 1 << 1
@@ -110,6 +110,9 @@ def load_library() -> ctypes.CDLL:
         "statekv_free_layer": (ctypes.c_int, [P]),
         "statekv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "statekv_select_topb": (ctypes.c_int, [P, ctypes.c_int32, ctypes.c_int32, P, P]),
+        "statekv_attention_mass": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int32),
+                                                  ctypes.c_int32, P, P, P]),
+        "statekv_mass_set_words": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int32)]),
         "statekv_profile_start": (ctypes.c_int, [P, ctypes.c_uint32, ctypes.c_int32]),
         "statekv_profile_stop": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -208,6 +211,19 @@ def statekv_select_topb(scores: int, n: int, budget: int, out_idx: int, stream: 
     _check(load_library().statekv_select_topb(scores, int(n), int(budget), out_idx,
                                               stream or None),
            "statekv_select_topb")
+
+
+def statekv_attention_mass(layer: int, budgets, sets: int, out: int, stream: int = 0) -> None:
+    arr = (ctypes.c_int32 * len(budgets))(*[int(b) for b in budgets])
+    _check(load_library().statekv_attention_mass(layer, arr, len(budgets), sets, out,
+                                                 stream or None), "statekv_attention_mass")
+
+
+def statekv_mass_set_words(layer: int) -> int:
+    w = ctypes.c_int32(0)
+    _check(load_library().statekv_mass_set_words(layer, ctypes.byref(w)),
+           "statekv_mass_set_words")
+    return w.value
 
 
 def statekv_profile_start(layer: int, kernel_mask: int, max_records: int) -> None:

@@ -32,6 +32,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "gather.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "rope.hip"),
+    os.path.join(CSRC, "kernels", "diagnostics.hip"),
 ]
 
 ARCH = "gfx950"

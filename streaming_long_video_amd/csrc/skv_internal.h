@@ -152,4 +152,19 @@ hipError_t launch_rope(const RopeArgs& r, int D, const Stream& st);
 
 hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st);
 
+// App. A diagnostics of the last frame (one workgroup per budget).
+constexpr int kMaxMassBudgets = 64;
+struct MassArgs {
+  const float* scores;  // [Hkv][ldscores] per-KV-head importance of the pool
+  int ldscores, Hkv;
+  int pool;             // tokens through the frame
+  int c;                // tokens of earlier frames
+  int have_prev;        // sets hold the previous frame's kept sets
+  uint32_t* sets;       // [n_budgets][ldsets] bit j of word j/32: token j kept
+  int ldsets;
+  float* out;           // [n_budgets][3]
+  int32_t budgets[kMaxMassBudgets];
+};
+hipError_t launch_attention_mass(const MassArgs& m, int n_budgets, const Stream& st);
+
 }  // namespace skv

@@ -435,6 +435,42 @@ int statekv_restore_layer(statekv_layer* L, int64_t frames_seen, int32_t count) 
   return STATEKV_OK;
 }
 
+int statekv_mass_set_words(const statekv_layer* L, int32_t* words) {
+  if (!L || !words) return STATEKV_ERR_INVALID_ARGUMENT;
+  *words = (L->plan.max_pool + 31) / 32;
+  return STATEKV_OK;
+}
+
+int statekv_attention_mass(statekv_layer* L, const int32_t* budgets, int32_t n_budgets,
+                           uint32_t* sets, float* out, void* stream) {
+  if (!L || !budgets || !sets || !out) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (n_budgets < 1 || n_budgets > skv::kMaxMassBudgets) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(sets) & 3u))
+    return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  // the last frame must have seen every token: no eviction so far
+  if (L->mode != 1 || L->n < 1 || L->last_pool <= 0) return STATEKV_ERR_INVALID_ARGUMENT;
+  if ((int64_t)L->last_pool != L->n * (int64_t)p.T) return STATEKV_ERR_INVALID_ARGUMENT;
+  skv::MassArgs m = {};
+  for (int i = 0; i < n_budgets; ++i) {
+    if (budgets[i] < 1) return STATEKV_ERR_INVALID_ARGUMENT;
+    m.budgets[i] = budgets[i];
+  }
+  m.scores = at<float>(L, p.off_scores);
+  m.ldscores = p.ldsig;
+  m.Hkv = p.Hkv;
+  m.pool = L->last_pool;
+  m.c = L->last_pool - p.T;
+  m.have_prev = L->n > 1;
+  m.sets = sets;
+  m.ldsets = (p.max_pool + 31) / 32;
+  m.out = out;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(timed(L, STATEKV_KERNEL_MASS, st, [&](const skv::Stream& ks) {
+    return skv::launch_attention_mass(m, n_budgets, ks);
+  }));
+}
+
 namespace {
 void destroy_profile_events(statekv_layer* L) {
   for (ProfRecord& r : L->prof) {

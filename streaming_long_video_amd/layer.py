@@ -102,6 +102,29 @@ class Layer:
                                    _stream_ptr(stream))
         return out
 
+    def attention_mass(self, budgets, sets=None, out=None, stream=None):
+        """App. A diagnostics of the last frame for a layer that has kept every
+        token (see statekv_attention_mass).  ``sets`` (int32 tensor of
+        len(budgets) x words, kept between calls; allocated zeroed when None)
+        carries each budget's kept set to the next call.  Returns (out, sets):
+        out is float32 [len(budgets)][3] = (top-b historical mass share,
+        recency share, weighted candidate-pool recall)."""
+        nb = len(budgets)
+        dev = self.workspace.device
+        words = B.statekv_mass_set_words(self.handle)
+        if sets is None:
+            sets = torch.zeros((nb, words), dtype=torch.int32, device=dev)
+        elif (sets.dtype != torch.int32 or tuple(sets.shape) != (nb, words)
+              or not sets.is_contiguous() or sets.device != dev):
+            raise ValueError(f"sets must be a contiguous int32 tensor of shape ({nb}, {words})")
+        if out is None:
+            out = torch.empty((nb, 3), dtype=torch.float32, device=dev)
+        elif out.dtype != torch.float32 or tuple(out.shape) != (nb, 3) or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor of shape (len(budgets), 3)")
+        B.statekv_attention_mass(self.handle, budgets, sets.data_ptr(), out.data_ptr(),
+                                 _stream_ptr(stream))
+        return out, sets
+
     # -- views -----------------------------------------------------------------
     def _ws_slice(self, ptr: int, nbytes: int, dtype, shape):
         off = ptr - self.workspace.data_ptr()

@@ -195,6 +195,30 @@ def test_restore_argument_errors_are_host_side():
     B.statekv_free_layer(h)
 
 
+def test_attention_mass_argument_errors_are_host_side():
+    """The App. A diagnostics need a frame that saw every token; bad budget
+    lists and pointers are refused before anything is launched."""
+    cfg = _cfg()  # T = 256, B = 4096
+    nbytes = B.statekv_workspace_bytes(cfg)
+    h = B.statekv_init_layer(cfg, 1 << 40, nbytes)
+    assert B.statekv_mass_set_words(h) == (4096 + 256 + 31) // 32
+    fake = 1 << 41
+    cases = [([], -1), ([0], -1), (list(range(1, 66)), -1),
+             ([1, 4], -1)]  # the last: no frame processed yet
+    for budgets, status in cases:
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_attention_mass(h, budgets, fake, fake)
+        assert e.value.status == status, budgets
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_attention_mass(h, [1], 0, fake)
+    assert e.value.status == -1
+    B.statekv_restore_layer(h, 3, 768)  # restored: the last frame's scores are gone
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_attention_mass(h, [1], fake, fake)
+    assert e.value.status == -1
+    B.statekv_free_layer(h)
+
+
 def test_select_argument_errors():
     with pytest.raises(B.StateKVError):
         B.statekv_select_topb(0, 10, 5, 0)
