@@ -3,8 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one frame through one layer: attention over [C_{n-1} ; frame]
-with importance scores, top-B select, gather of C_n and append to D (every
-row of the hot path).  Default workload: the InternVL3-8B-like layer
+with importance scores, top-B select, the state update C_n and the append to
+D (every row of the hot path).  By default C is updated in place (kept rows
+stay, kept frame tokens fill the freed rows; --state-layout rows rewrites C_n
+in position order with a separate gather launch).  Default workload: the InternVL3-8B-like layer
 (Hq=28, Hkv=4, d=128, T=256, B=4096), W=16 warm-up frames (they fill the
 state: 16*256 = B) and K=496 timed frames, i.e. the pages' 512-frame stream.
 All frames are generated on the host (seeded, synthetic) and staged in HBM
@@ -25,6 +27,9 @@ Other measurements (not the headline line):
     --mode decode      decoding attention over the detailed state after the
                        512-frame 8B stream (1 and 4 text tokens): time per
                        call and HBM bandwidth of the decode kernel
+    --mode mass        App. A diagnostics (top-b historical mass, recency
+                       mass, candidate-pool recall) of a layer that keeps
+                       every token, averaged over --mass-frames frames
 """
 
 from __future__ import annotations
@@ -512,7 +517,7 @@ def main(argv=None):
                          "(reference kernel for rocprofv3 byte counters)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = auto)")
     ap.add_argument("--state-layout", choices=["rows", "positions", "inplace", "inplace-positions"],
-                    default="rows",
+                    default="inplace",
                     help="C as its own K/V rows rewritten on update (rows), as positions into "
                          "D (positions), updated in place (inplace), or both")
     ap.add_argument("--mass-frames", type=int, default=64,

@@ -52,6 +52,13 @@ COMMON = [
 ]
 
 
+# per-source flags: the attention kernels take finite inputs, so the row
+# maxima need no NaN-quieting of their operands
+EXTRA = {
+    os.path.join(CSRC, "kernels", "attention.hip"): ["-fno-honor-nans"],
+}
+
+
 def _obj(src: str) -> str:
     rel = os.path.relpath(src, CSRC).replace(os.sep, "_")
     return os.path.join(BUILD, rel + ".o")
@@ -76,7 +83,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     cmds = []
     for src in SOURCES:
         lang = [] if src.endswith(".cpp") else ["-x", "hip"]
-        cmds.append([HIPCC, *COMMON, *lang, "-c", src, "-o", _obj(src)])
+        cmds.append([HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", src, "-o", _obj(src)])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
