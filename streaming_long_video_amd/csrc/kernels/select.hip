@@ -141,16 +141,22 @@ __host__ __device__ inline bool in_place_lds_fits(int pool, int T) {
 // rows (K and V rows, 16-byte chunks, up to kMoveU loads in flight per
 // thread) and writes their positions.  Move r goes to row mv[r] and comes
 // from frame token mv[T + r]; mv null: rows c + r from token r (the frame is
-// appended while C fills).
+// appended while C fills).  A move whose row or token lies outside C or the
+// frame is skipped: the lists never hold one, and a broken list must not turn
+// into stores outside the state.
 constexpr int kMoveU = 8;
 __device__ void apply_moves(const InPlace& ip, const int32_t* mv, int M, int h0, int h1) {
   const int tid = threadIdx.x;
   const int nh = h1 - h0;
   auto dst_of = [&](int r) { return mv ? mv[r] : ip.c + r; };
   auto src_of = [&](int r) { return mv ? mv[ip.T + r] : r; };
+  auto valid = [&](int d, int t) {
+    return (unsigned)d < (unsigned)ip.ldpos && (unsigned)t < (unsigned)ip.T;
+  };
   for (int i = tid; i < nh * M; i += kSelThreads) {
     const int h = h0 + i / M, r = i % M;
-    ip.pos[(int64_t)h * ip.ldpos + dst_of(r)] = ip.frame_pos0 + src_of(r);
+    const int d = dst_of(r), t = src_of(r);
+    if (valid(d, t)) ip.pos[(int64_t)h * ip.ldpos + d] = ip.frame_pos0 + t;
   }
   if (!ip.kc) return;  // the state is kept as positions into D
   const int CH = ip.D / 8;
@@ -168,9 +174,12 @@ __device__ void apply_moves(const InPlace& ip, const int32_t* mv, int M, int h0,
         const int which = (int)(rest & 1);
         const int64_t mr = rest >> 1;
         const int h = h0 + (int)(mr / M), r = (int)(mr % M);
-        const int64_t src = ((int64_t)src_of(r) * ip.Hkv + h) * ip.D + ch * 8;
-        buf[u] = *reinterpret_cast<const u32x4*>((which ? ip.vf : ip.kf) + src);
-        dst[u] = (which ? ip.vc : ip.kc) + ((int64_t)h * ip.ldpos + dst_of(r)) * ip.D + ch * 8;
+        const int d = dst_of(r), t = src_of(r);
+        if (valid(d, t)) {
+          const int64_t src = ((int64_t)t * ip.Hkv + h) * ip.D + ch * 8;
+          buf[u] = *reinterpret_cast<const u32x4*>((which ? ip.vf : ip.kf) + src);
+          dst[u] = (which ? ip.vc : ip.kc) + ((int64_t)h * ip.ldpos + d) * ip.D + ch * 8;
+        }
       }
     }
 #pragma unroll
