@@ -96,12 +96,15 @@ __device__ inline float dpp_all(float src) {
 
 // Sum of v[r] over the 32 lanes of each half-wave (the 32 queries of a block),
 // reduce-scatter style.  Lane l ends with the total of register r = (l>>1)&15
-// (both lanes of a pair hold it).
+// (both lanes of a pair hold it).  Each stage halves the registers a lane
+// keeps: the lane picks its own half and the partner's copy of it arrives by
+// one DPP read folded into the add.
 //   xor 16: v_permlane16_swap pairs (v[k], v[k+8]) across 16-lane rows;
-//   xor 8:  row_ror:8 into banks {0,1} / {2,3};
-//   xor 4:  row_shl:4 into banks {0,2}, row_shr:4 into banks {1,3};
-//   xor 2, xor 1: quad_perm.
+//   bit 3:  row_ror:8 (lane i <-> i^8 in a row), keep w[k + 4 b3];
+//   bit 2:  row_half_mirror (lane i <-> 7-i in 8 lanes), keep x[k + 2 b2];
+//   bit 1, bit 0: quad_perm xor 2, xor 1.
 __device__ inline float colsum_reduce(const float (&v)[16], int l32) {
+  const bool b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
   float w[8], x[4], y[2];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -110,20 +113,16 @@ __device__ inline float colsum_reduce(const float (&v)[16], int l32) {
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const float t = dpp_into<0x128, 0x3>(w[k + 4], w[k]);
-    const float u = dpp_into<0x128, 0xC>(w[k], w[k + 4]);
-    x[k] = t + u;  // r = 8*b4 + 4*b3 + k
+    const float keep = b3 ? w[k + 4] : w[k], give = b3 ? w[k] : w[k + 4];
+    x[k] = keep + dpp_all<0x128>(give);  // r = 8*b4 + 4*b3 + k
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const float t = dpp_into<0x104, 0x5>(x[k + 2], x[k]);
-    const float u = dpp_into<0x114, 0xA>(x[k], x[k + 2]);
-    y[k] = t + u;  // r = 8*b4 + 4*b3 + 2*b2 + k
+    const float keep = b2 ? x[k + 2] : x[k], give = b2 ? x[k] : x[k + 2];
+    y[k] = keep + dpp_all<0x141>(give);  // r = 8*b4 + 4*b3 + 2*b2 + k
   }
-  // cross-lane reads must run with every lane active: both before the select
-  const float p0 = dpp_all<0x4E>(y[0]);
-  const float p1 = dpp_all<0x4E>(y[1]);
-  const float z = (l32 & 2) ? y[1] + p1 : y[0] + p0;
+  const float keep = b1 ? y[1] : y[0], give = b1 ? y[0] : y[1];
+  const float z = keep + dpp_all<0x4E>(give);
   return z + dpp_all<0xB1>(z);
 }
 
@@ -538,6 +537,10 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
 #pragma unroll
         for (int m = 0; m < 4; ++m)
           ph[i][slab][m] = pack_f16(p[i][slab * 8 + 2 * m], p[i][slab * 8 + 2 * m + 1]);
+    // the column-sum swaps overwrite their operands: the packs are formed first
+    // (an empty asm that reads them), so no copies of P are needed
+#pragma unroll
+    for (int i = 0; i < QB; ++i) asm volatile("" ::"v"(ph[i][0]), "v"(ph[i][1]));
     float cs[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
