@@ -1,6 +1,7 @@
 """The InternVL3-8B-like layer at full size (Hq=28, Hkv=4, d=128, T=256,
 B=4096, 512 frames, D preallocated for 131072 tokens), in the launch
-configuration the benchmark times.  The oracle checks sampled frames one by
+configuration the benchmark times (the in-place state update) and with the
+position-ordered gather.  The oracle checks sampled frames one by
 one from the GPU's own state (teacher forced); properties that hold at any
 size are checked on every frame."""
 
@@ -35,11 +36,19 @@ def _oracle_sinks_kept(golden, h, n, T):
                   if int(s) < (n + 1) * T and (f is None or f > n))
 
 
-def test_8b_layer_512_frames():
+@pytest.fixture(scope="module")
+def frames_8b():
     spec = framegen.workload("internvl3_8b_layer")
-    qs, ks, vs = framegen.stacked_frames(spec, workers=16)
+    return spec, framegen.stacked_frames(spec, workers=16)
+
+
+@pytest.mark.parametrize("layout", ["inplace", "rows"])
+def test_8b_layer_512_frames(frames_8b, layout):
+    spec, (qs, ks, vs) = frames_8b
+    flags = skv.STATEKV_FLAG_SLOT_STABLE if layout == "inplace" else 0
     layer = skv.Layer(spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.frame_tokens,
-                      spec.state_budget, detailed_capacity=spec.n_frames * spec.frame_tokens)
+                      spec.state_budget, detailed_capacity=spec.n_frames * spec.frame_tokens,
+                      flags=flags)
     orc = StateKVOracle(spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.frame_tokens,
                         spec.state_budget)
     _, sinks = framegen.sink_plan(spec)
