@@ -152,13 +152,15 @@ def test_state_kept_as_positions_into_d(flags):
         np.testing.assert_array_equal(snapshot(a).pos[0], snapshot(b).pos[0])
 
 
-@pytest.mark.parametrize("flags", [0, "ring", "c_in_d"])
+@pytest.mark.parametrize("flags", [0, "ring", "c_in_d", "in_place", "in_place_c_in_d"])
 def test_checkpoint_and_restore(flags):
     """A layer checkpointed after 6 frames (C rows and positions, D, frames
     seen) and restored into a fresh layer continues bit-identically."""
     spec = framegen.workload("internvl3_1b_layer").replace(n_frames=12)
     qs, ks, vs = framegen.stacked_frames(spec, workers=8)
-    f = {0: 0, "ring": skv.STATEKV_FLAG_D_RING, "c_in_d": skv.STATEKV_FLAG_C_IN_D}[flags]
+    f = {0: 0, "ring": skv.STATEKV_FLAG_D_RING, "c_in_d": skv.STATEKV_FLAG_C_IN_D,
+         "in_place": skv.STATEKV_FLAG_SLOT_STABLE,
+         "in_place_c_in_d": skv.STATEKV_FLAG_SLOT_STABLE | skv.STATEKV_FLAG_C_IN_D}[flags]
     cap = (8 if flags == "ring" else 12) * spec.frame_tokens
     a = _layer(spec, flags=f, detailed_capacity=cap)
     b = _layer(spec, flags=f, detailed_capacity=cap)
