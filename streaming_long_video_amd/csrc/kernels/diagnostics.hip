@@ -159,14 +159,9 @@ __global__ __launch_bounds__(kDiagThreads) void attention_mass_kernel(MassArgs m
 }
 
 hipError_t launch_attention_mass(const MassArgs& m, int n_budgets, const Stream& st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attention_mass_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kMaxPool * (int)sizeof(float));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(attention_mass_kernel), kMaxPool * (int)sizeof(float), lds_set);
+  if (e != hipSuccess) return e;
   hipExtLaunchKernelGGL(attention_mass_kernel, dim3(n_budgets), dim3(kDiagThreads),
                         (size_t)m.pool * sizeof(float), st.st, st.start, st.stop, 0, m);
   return hipGetLastError();

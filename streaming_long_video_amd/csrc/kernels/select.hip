@@ -501,14 +501,9 @@ namespace {
 hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& J2, int n_shared,
                              const AppendJob& A, int n_append, const SumJob& Sj, int sum_blocks,
                              const Stream& st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_sum_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kMaxPool * (int)sizeof(uint32_t));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(select_sum_kernel), kMaxPool * (int)sizeof(uint32_t), lds_set);
+  if (e != hipSuccess) return e;
   size_t words = (size_t)J.pool;
   if ((J.ip.pos || J2.ip.pos) && in_place_lds_fits(J.pool, J.ip.T))
     words = (size_t)J.pool + 2 * (size_t)J.ip.T;
@@ -532,10 +527,17 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
   SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
                S};
+  // The O sum runs beside the selection, which is the launch's long pole:
+  // few workgroups with several outputs per thread leave the selecting
+  // workgroups more of the memory system, as long as the sum still ends
+  // first.  Measured at the 8B-like shape: 3.5 f32x4 outputs per thread (64
+  // workgroups) when the selecting workgroups also move rows in place, 1.75
+  // (128) otherwise, each 1.5-2 us faster than one output per thread.
   int sum_blocks = 0;
   if (o_part && S > 1 && o_elems > 0) {
-    const int64_t want = (Sj.n4 + kSelThreads - 1) / kSelThreads;
-    sum_blocks = (int)(want < 1024 ? want : 1024);
+    const int64_t per2 = ip.pos ? 7 : 4;  // twice the outputs per thread, rounded
+    const int64_t want = (2 * Sj.n4 + per2 * kSelThreads - 1) / (per2 * kSelThreads);
+    sum_blocks = (int)(want < 64 ? 64 : want > 1024 ? 1024 : want);
   }
   AppendJob A = {};
   int n_append = 0;

@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "plan.h"
 
 namespace skv {
@@ -17,6 +19,19 @@ struct Stream {
   Stream(hipStream_t s) : st(s) {}  // NOLINT: plain streams convert implicitly
   Stream(hipStream_t s, hipEvent_t a, hipEvent_t b) : st(s), start(a), stop(b) {}
 };
+
+// Raises the dynamic-LDS limit of kernel `fn` to `bytes` on the current
+// device, once per device (safe to call from several host threads).
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // Arguments of the two attention passes over the pool [C_{n-1} ; frame].
 struct AttnArgs {
