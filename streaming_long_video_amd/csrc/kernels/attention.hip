@@ -71,7 +71,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 __host__ __device__ constexpr int vt_pos(int k) {
   return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
-constexpr float kPUnscale = 1.f / 4096.f;  // P is formed as 2^12 * P
+constexpr float kPUnscale = kOPartUnscale;  // P is formed as 2^12 * P
 
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each
 // XCD gets a contiguous range of logical ids (consecutive ids share a KV head
@@ -400,31 +400,39 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
       static_assert(kThreads == 2 * kRowBlk * kTokBlk, "two threads per row");
       constexpr int kGrp = 16;
       __shared__ float mh[2][kRowBlk * kTokBlk], lh[2][kRowBlk * kTokBlk];
-      const int r = tid % (kRowBlk * kTokBlk), par = tid / (kRowBlk * kTokBlk);
+      // par is uniform over a wave: the split offsets below are scalar
+      const int r = tid % (kRowBlk * kTokBlk);
+      const int par = __builtin_amdgcn_readfirstlane(tid / (kRowBlk * kTokBlk));
       const int b = b0 + r / kTokBlk;
       const int t = (b / a.G) * kTokBlk + r % kTokBlk;
       float M = -INFINITY, L = 0.f;
       if (b < a.nqblk && t < a.T) {
-        const int64_t stride = (int64_t)a.Hq * a.tpad;
-        const float* mp = a.m_part + (int64_t)(h * a.G + b % a.G) * a.tpad + t;
-        const float* lp = a.l_part + (int64_t)(h * a.G + b % a.G) * a.tpad + t;
+        // 32-bit offsets (the partials hold Sst * Hq * tpad floats); loads
+        // past the last split re-read it and are then replaced, so no load is
+        // conditional; exp2 of -inf (an empty split) is 0
+        const int stride = a.Hq * a.tpad, last = a.Sst - 1;
+        const uint32_t rbytes = (uint32_t)((h * a.G + b % a.G) * a.tpad + t) * 4u;
         for (int s0 = par; s0 < a.Sst; s0 += 2 * kGrp) {
           float mv[kGrp], lv[kGrp];
 #pragma unroll
           for (int u = 0; u < kGrp; ++u) {
             const int sp = s0 + 2 * u;
-            const bool in = sp < a.Sst;
-            mv[u] = in ? mp[sp * stride] : -INFINITY;
-            lv[u] = in ? lp[sp * stride] : 0.f;
+            const int o = min(sp, last) * stride;
+            // scalar base + 32-bit lane offset: one address register for all loads
+            const float mr = *reinterpret_cast<const float*>(
+                reinterpret_cast<const char*>(a.m_part + o) + rbytes);
+            const float lr = *reinterpret_cast<const float*>(
+                reinterpret_cast<const char*>(a.l_part + o) + rbytes);
+            mv[u] = sp <= last ? mr : -INFINITY;
+            lv[u] = sp <= last ? lr : 0.f;
           }
           float Mg = M;
 #pragma unroll
           for (int u = 0; u < kGrp; ++u) Mg = fmaxf(Mg, mv[u]);
           const float Ms = Mg == -INFINITY ? 0.f : Mg;
-          L = M == -INFINITY ? 0.f : L * exp2f((M - Ms) * sl2);
+          L = L * __builtin_amdgcn_exp2f((M - Ms) * sl2);
 #pragma unroll
-          for (int u = 0; u < kGrp; ++u)
-            if (mv[u] > -INFINITY) L += lv[u] * exp2f((mv[u] - Ms) * sl2);
+          for (int u = 0; u < kGrp; ++u) L += lv[u] * __builtin_amdgcn_exp2f((mv[u] - Ms) * sl2);
           M = Mg;
         }
       }
@@ -690,19 +698,26 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
     // key tiles of this split that no query of the row tile can see
     for (int j = tile_end * KT + tid; j < min(tile_hi * KT, pool); j += kThreads)
       a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = 0.f;
-    // O^T[d = 32mb + 8(r/4) + 4 half + r%4][query] -> O[t][g][d]
+    // O^T[d = 32mb + 8(r/4) + 4 half + r%4][query] -> O[t][g][d]; split
+    // partials keep P's 2^12 (the sum of the splits removes it), a single
+    // split is the output itself
+    const float oscale = a.S == 1 ? kPUnscale : 1.f;
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
       if (qtok[i] < 0) continue;
       float* dst = a.o_out + ((int64_t)(a.S == 1 ? 0 : s) * a.T + qtok[i]) * a.Hq * D +
                    (int64_t)qhead[i] * D;
+      if (a.S == 1) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= oscale;
+      }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
                      oacc[i][mb][4 * q4 + 3]};
-          *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * q4 + 4 * half) = v * kPUnscale;
+          *reinterpret_cast<f32x4*>(dst + mb * 32 + 8 * q4 + 4 * half) = v;
         }
     }
   } else if constexpr (PASS == 3) {

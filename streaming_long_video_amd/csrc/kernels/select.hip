@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
        i += nb * kSelThreads) {
     f32x4 acc = Sj.part[i];
     for (int s = 1; s < Sj.S; ++s) acc += Sj.part[s * Sj.n4 + i];
-    Sj.out[i] = acc;
+    Sj.out[i] = acc * kOPartUnscale;
   }
 }
 
