@@ -213,7 +213,7 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   // every load of a batch (kLoad candidates x kRows row tiles per thread) is
   // in flight at once
   constexpr int kLoad = 5;  // 5 * 1024 >= 4352: one round at the 8B-like shape
-  constexpr int kRows = 4;
+  constexpr int kRows = 8;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int j0 = 0; j0 < pool; j0 += kLoad * kSelThreads) {
     float acc[kLoad];
@@ -222,12 +222,15 @@ __device__ void select_one_head(const SelectJob& J, int h) {
     for (int r0 = 0; r0 < J.rt; r0 += kRows) {
       float part[kRows][kLoad];
 #pragma unroll
-      for (int u = 0; u < kRows; ++u)
+      for (int u = 0; u < kRows; ++u) {
+        // the row's base is uniform, each lane adds a 32-bit byte offset
+        const char* row = reinterpret_cast<const char*>(sp + (int64_t)min(r0 + u, J.rt - 1) * J.ldsig);
 #pragma unroll
         for (int q = 0; q < kLoad; ++q) {
-          const int j = min(j0 + tid + q * kSelThreads, pool - 1);
-          part[u][q] = r0 + u < J.rt ? sp[(int64_t)(r0 + u) * J.ldsig + j] : 0.f;
+          const uint32_t j = (uint32_t)min(j0 + tid + q * kSelThreads, pool - 1);
+          part[u][q] = *reinterpret_cast<const float*>(row + j * 4u);
         }
+      }
 #pragma unroll
       for (int u = 0; u < kRows; ++u)
 #pragma unroll
