@@ -473,9 +473,10 @@ int statekv_attention_mass(statekv_layer* L, const int32_t* budgets, int32_t n_b
 
 namespace {
 void destroy_profile_events(statekv_layer* L) {
+  // teardown: a failed destroy leaves nothing to recover
   for (ProfRecord& r : L->prof) {
-    hipEventDestroy(r.before);
-    hipEventDestroy(r.after);
+    (void)hipEventDestroy(r.before);
+    (void)hipEventDestroy(r.after);
   }
   L->prof.clear();
   L->prof_used = 0;
@@ -495,7 +496,7 @@ int statekv_profile_start(statekv_layer* L, uint32_t kernel_mask, int32_t max_re
       return STATEKV_ERR_HIP;
     }
     if (hipEventCreate(&r.after) != hipSuccess) {
-      hipEventDestroy(r.before);
+      (void)hipEventDestroy(r.before);
       destroy_profile_events(L);
       return STATEKV_ERR_HIP;
     }
