@@ -99,6 +99,10 @@ int main() {
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_INVALID_ARGUMENT);
   c = cfg(28, 4, 128, 256, 32600, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
+  c = cfg(28, 4, 128, 256, 32512, 131072);  // B + T = 32768: the largest pool
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.max_pool == 32768);
+  c = cfg(28, 4, 128, 256, 32513, 131072);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
   c = cfg(34, 2, 128, 256, 4096, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
   c = cfg(28, 4, 128, 0, 4096, 131072);

@@ -319,6 +319,17 @@ def test_in_place_large_frame(d, shared):
     check_caches_bitwise(layer, ks, vs)
 
 
+@pytest.mark.parametrize("in_place", [False, True])
+def test_largest_pool(in_place):
+    """B + T = 32768, the largest pool the select keeps in LDS (T = 4096, B =
+    28672): nine frames, the last two evicting; teacher-forced."""
+    spec = framegen.FrameSpec(1, 1, 64, 4096, 9, 28672, 1e4, 23, sinks=False)
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SLOT_STABLE if in_place else 0)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec, layer=layer)
+    _assert_reports(reports, exact_select=False)
+    check_caches_bitwise(layer, ks, vs)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 5])
 def test_explicit_split_counts(splits):
     spec = framegen.workload("tiny").replace(n_q_heads=4, n_kv_heads=2, frame_tokens=48,
