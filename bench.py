@@ -97,6 +97,23 @@ def gather_bytes(Hkv, d, T, B, c, rows=True) -> float:
     return float(gather + append)
 
 
+def select_bytes(Hkv, Hq, d, T, B, c, plan, in_place) -> float:
+    """The select launch's bytes that must cross HBM once (state moves excluded:
+    at most Hkv*T rows, data-dependent).
+
+    Read the row tiles' score partials and write the scores; write the
+    selection (kept indices, or in place the move lists); when the output pass
+    ran in several key splits, read their O partials and write O; in place,
+    also the D append (read the frame's K and V rows, write them to D)."""
+    pool = c + T
+    scores = Hkv * plan["row_tiles"] * pool * 4 + Hkv * pool * 4
+    sel = Hkv * (2 * T + 1 if in_place else min(B, pool)) * 4
+    S = plan["out_splits"]
+    osum = (S + 1) * T * Hq * d * 4 if S > 1 else 0
+    append = Hkv * T * 2 * (2 * d * 2) if in_place else 0
+    return float(scores + sel + osum + append)
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on host cores
 # ----------------------------------------------------------------------------
@@ -280,6 +297,17 @@ def run_headline(args):
             "bytes_per_launch": gb, "avg_launch_us": tg,
             "achieved_gbs": gb / (tg * 1e-6) / 1e9,
             "frac_of_hbm_peak": gb / (tg * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        }
+    if breakdown_us.get("select"):
+        in_place = args.state_layout.startswith("inplace")
+        sb = float(np.mean([select_bytes(Hkv, Hq, d, T, Bs, c, layer.launch_plan(c + T), in_place)
+                            for c in cs]))
+        ts = breakdown_us["select"]
+        result["select_launch"] = {
+            "bytes_per_launch": sb, "avg_launch_us": ts,
+            "achieved_gbs": sb / (ts * 1e-6) / 1e9,
+            "frac_of_hbm_peak": sb / (ts * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "includes": "score sums, selection, O split sum" + (", D append" if in_place else ""),
         }
     result["kernels_us"] = {k: v for k, v in breakdown_us.items()}
     result["kernels_us_frames"] = f"{W + K}..{W + K + KB - 1}" if KB > 0 else "timed frames"

@@ -260,6 +260,21 @@ int statekv_attention_mass(statekv_layer* layer, const int32_t* budgets,
 /* Words per budget of the sets buffer of statekv_attention_mass (host only). */
 int statekv_mass_set_words(const statekv_layer* layer, int32_t* words);
 
+/* The launch plan of the prefill step at a pool of `pool` candidates (c + T,
+ * 1 <= pool <= B + T): the key splits of the output pass (each writes one fp32
+ * O partial, summed in the select launch) and of the statistics pass, the row
+ * tiles of one KV head's G*T query rows (256 rows each) and the pool's 64-key
+ * tiles.  For callers that size or measure the step's traffic; host only, no
+ * device work.  STATEKV_ERR_INVALID_ARGUMENT for a null argument or a pool out
+ * of range. */
+typedef struct {
+  int32_t out_splits;   /* key splits of the output pass                      */
+  int32_t stat_splits;  /* key splits of the statistics pass                  */
+  int32_t row_tiles;    /* 256-row tiles per KV head                          */
+  int32_t key_tiles;    /* ceil(pool / 64)                                    */
+} statekv_launch_plan;
+int statekv_launch_plan_for(const statekv_layer* layer, int32_t pool, statekv_launch_plan* out);
+
 /* Release the host handle (the workspace stays the caller's). */
 int statekv_free_layer(statekv_layer* layer);
 

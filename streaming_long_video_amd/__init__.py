@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     statekv_full_attention_frame,
     statekv_init_layer,
     statekv_mass_set_words,
+    statekv_launch_plan_for,
     statekv_prefill_frame,
     statekv_profile_start,
     statekv_profile_stop,

@@ -82,6 +82,15 @@ class statekv_cache_view(ctypes.Structure):
     ]
 
 
+class statekv_launch_plan(ctypes.Structure):
+    _fields_ = [
+        ("out_splits", ctypes.c_int32),
+        ("stat_splits", ctypes.c_int32),
+        ("row_tiles", ctypes.c_int32),
+        ("key_tiles", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -113,6 +122,8 @@ def load_library() -> ctypes.CDLL:
         "statekv_attention_mass": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int32),
                                                   ctypes.c_int32, P, P, P]),
         "statekv_mass_set_words": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int32)]),
+        "statekv_launch_plan_for": (ctypes.c_int, [P, ctypes.c_int32,
+                                                   ctypes.POINTER(statekv_launch_plan)]),
         "statekv_profile_start": (ctypes.c_int, [P, ctypes.c_uint32, ctypes.c_int32]),
         "statekv_profile_stop": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -217,6 +228,14 @@ def statekv_attention_mass(layer: int, budgets, sets: int, out: int, stream: int
     arr = (ctypes.c_int32 * len(budgets))(*[int(b) for b in budgets])
     _check(load_library().statekv_attention_mass(layer, arr, len(budgets), sets, out,
                                                  stream or None), "statekv_attention_mass")
+
+
+def statekv_launch_plan_for(layer: int, pool: int) -> dict:
+    """The prefill step's launch plan at a pool of `pool` candidates."""
+    lp = statekv_launch_plan()
+    _check(load_library().statekv_launch_plan_for(layer, int(pool), ctypes.byref(lp)),
+           "statekv_launch_plan_for")
+    return {f: int(getattr(lp, f)) for f, _ in statekv_launch_plan._fields_}
 
 
 def statekv_mass_set_words(layer: int) -> int:

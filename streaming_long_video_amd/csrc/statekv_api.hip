@@ -435,6 +435,16 @@ int statekv_restore_layer(statekv_layer* L, int64_t frames_seen, int32_t count) 
   return STATEKV_OK;
 }
 
+int statekv_launch_plan_for(const statekv_layer* L, int32_t pool, statekv_launch_plan* out) {
+  if (!L || !out || pool < 1 || pool > L->plan.max_pool) return STATEKV_ERR_INVALID_ARGUMENT;
+  const skv::Plan& p = L->plan;
+  out->out_splits = skv::splits_for_pool(p, pool);
+  out->stat_splits = skv::stat_splits_for_pool(p, pool);
+  out->row_tiles = p.rt;
+  out->key_tiles = (pool + skv::kKeyTile - 1) / skv::kKeyTile;
+  return STATEKV_OK;
+}
+
 int statekv_mass_set_words(const statekv_layer* L, int32_t* words) {
   if (!L || !words) return STATEKV_ERR_INVALID_ARGUMENT;
   *words = (L->plan.max_pool + 31) / 32;

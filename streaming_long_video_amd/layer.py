@@ -102,6 +102,10 @@ class Layer:
                                    _stream_ptr(stream))
         return out
 
+    def launch_plan(self, pool: int) -> dict:
+        """Split and tile counts of the prefill step at a pool of `pool` candidates."""
+        return B.statekv_launch_plan_for(self.handle, pool)
+
     def attention_mass(self, budgets, sets=None, out=None, stream=None):
         """App. A diagnostics of the last frame for a layer that has kept every
         token (see statekv_attention_mass).  ``sets`` (int32 tensor of

@@ -330,6 +330,20 @@ def test_largest_pool(in_place):
     check_caches_bitwise(layer, ks, vs)
 
 
+def test_launch_plan_introspection():
+    """The plan the step runs at the 8B shape: 9 output splits, 18 statistics
+    splits, 7 row tiles, 68 key tiles at the full pool; at a one-frame pool
+    no split is emptier than a tile; pools outside [1, B+T] are refused."""
+    layer = skv.Layer(28, 4, 128, 256, 4096, detailed_capacity=4096)
+    assert layer.launch_plan(4352) == {"out_splits": 9, "stat_splits": 18, "row_tiles": 7,
+                                       "key_tiles": 68}
+    small = layer.launch_plan(256)
+    assert small["key_tiles"] == 4 and small["out_splits"] <= 4 and small["stat_splits"] <= 4
+    for bad in (0, 4353):
+        with pytest.raises(skv.StateKVError):
+            layer.launch_plan(bad)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 5])
 def test_explicit_split_counts(splits):
     spec = framegen.workload("tiny").replace(n_q_heads=4, n_kv_heads=2, frame_tokens=48,
