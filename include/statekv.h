@@ -95,7 +95,12 @@ enum {
    * position order (the state view's pos gives each row's position); ties in
    * importance still go to the lower original position, as long as the
    * positions of the tied candidates lie within 2^32 - 3 of the newest one. */
-  STATEKV_FLAG_SLOT_STABLE = 1u << 5
+  STATEKV_FLAG_SLOT_STABLE = 1u << 5,
+  /* statekv_prefill_frame writes O as bf16 [T][Hq][d] (round to nearest even
+   * from the fp32 result it would otherwise write) instead of fp32, for a
+   * caller that feeds O to a bf16 output projection.  The quadratic baseline
+   * (statekv_full_attention_frame) refuses such a layer. */
+  STATEKV_FLAG_OUT_BF16 = 1u << 6
 };
 
 typedef struct statekv_layer statekv_layer; /* opaque, host memory */
@@ -177,7 +182,7 @@ int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace,
  * gather + detailed-cache append (with SLOT_STABLE the select launch applies
  * the state update and the append itself: three launches). */
 int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
-                          const void* v, float* o, void* stream);
+                          const void* v, void* o, void* stream);
 
 /* Quadratic baseline on the same layer object (full causal self-attention, the
  * pages' "Full SA"): appends the frame to D, then the frame's queries attend

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     STATEKV_FLAG_SELECT_RECENT,
     STATEKV_FLAG_SELECT_SHARED,
     STATEKV_FLAG_SLOT_STABLE,
+    STATEKV_FLAG_OUT_BF16,
     STATEKV_KERNELS,
     StateKVError,
     load_library,

@@ -29,6 +29,7 @@ STATEKV_FLAG_NONCAUSAL_FRAME = 1 << 2
 STATEKV_FLAG_C_IN_D = 1 << 3
 STATEKV_FLAG_SELECT_RECENT = 1 << 4
 STATEKV_FLAG_SLOT_STABLE = 1 << 5
+STATEKV_FLAG_OUT_BF16 = 1 << 6
 
 
 class StateKVError(RuntimeError):

@@ -44,6 +44,7 @@
 namespace skv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -710,6 +711,19 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
       if (a.S == 1) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= oscale;
+      }
+      if (a.S == 1 && a.out_bf16) {  // the output itself, as bf16 (same element offsets)
+        __bf16* dst16 = reinterpret_cast<__bf16*>(a.o_out) + ((int64_t)qtok[i] * a.Hq + qhead[i]) * D;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
+                       oacc[i][mb][4 * q4 + 3]};
+            *reinterpret_cast<bf16x4*>(dst16 + mb * 32 + 8 * q4 + 4 * half) =
+                __builtin_convertvector(v, bf16x4);
+          }
+        continue;
       }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)

@@ -190,10 +190,13 @@ __device__ void apply_moves(const InPlace& ip, const int32_t* mv, int M, int h0,
 
 struct SumJob {
   const f32x4* part;      // [S][n4]
-  f32x4* out;             // [n4]
+  void* out;              // [n4] f32x4, or [n4] x 4 bf16 when bf16
   int64_t n4;
   int S;
+  int bf16;
 };
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ void select_one_head(const SelectJob& J, int h) {
   extern __shared__ uint32_t keys[];
@@ -496,7 +499,11 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
        i += nb * kSelThreads) {
     f32x4 acc = Sj.part[i];
     for (int s = 1; s < Sj.S; ++s) acc += Sj.part[s * Sj.n4 + i];
-    Sj.out[i] = acc * kOPartUnscale;
+    acc *= kOPartUnscale;
+    if (Sj.bf16)
+      static_cast<bf16x4*>(Sj.out)[i] = __builtin_convertvector(acc, bf16x4);
+    else
+      static_cast<f32x4*>(Sj.out)[i] = acc;
   }
 }
 
@@ -520,7 +527,8 @@ hipError_t launch_select_sum(const SelectJob& J, int n_select, const SelectJob& 
 
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool, int budget,
                          float* scores, int ldscores, int32_t* sel, int ldsel,
-                         const float* o_part, int S, int64_t o_elems, float* o, bool shared,
+                         const float* o_part, int S, int64_t o_elems, void* o, bool o_bf16,
+                         bool shared,
                          bool recent, const InPlace& ip, const AppendJob* app,
                          const Stream& st) {
   shared = shared && !recent;  // the recency window is the same for every head
@@ -528,8 +536,7 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
                  ldsel, recent ? 1 : 0, ip, 0};
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
   SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
-  SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), reinterpret_cast<f32x4*>(o), o_elems / 4,
-               S};
+  SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0};
   // The O sum runs beside the selection, which is the launch's long pole:
   // few workgroups with several outputs per thread leave the selecting
   // workgroups more of the memory system, as long as the sum still ends

@@ -24,7 +24,8 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   if (cfg->num_splits < 0) return STATEKV_ERR_INVALID_ARGUMENT;
   if (cfg->flags & ~(uint32_t)(STATEKV_FLAG_SELECT_SHARED | STATEKV_FLAG_D_RING |
                                STATEKV_FLAG_NONCAUSAL_FRAME | STATEKV_FLAG_C_IN_D |
-                               STATEKV_FLAG_SELECT_RECENT | STATEKV_FLAG_SLOT_STABLE))
+                               STATEKV_FLAG_SELECT_RECENT | STATEKV_FLAG_SLOT_STABLE |
+                               STATEKV_FLAG_OUT_BF16))
     return STATEKV_ERR_INVALID_ARGUMENT;
   if ((cfg->flags & STATEKV_FLAG_C_IN_D) && (cfg->flags & STATEKV_FLAG_D_RING))
     return STATEKV_ERR_UNSUPPORTED;

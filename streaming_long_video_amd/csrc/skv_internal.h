@@ -43,6 +43,7 @@ struct AttnArgs {
   float* m_part;       // [Sst][Hq][tpad] per-split row max of raw logits
   float* l_part;       // [Sst][Hq][tpad] per-split sum of exp relative to m
   float* o_out;        // [T][Hq][D] fp32 when S == 1, else [S][T][Hq][D] partials
+  int out_bf16;        // S == 1: o_out holds [T][Hq][D] bf16 instead
   float* sig_part;     // [Hkv][rt][ldsig] per-row-tile score partials
   int64_t ldc;         // state rows per KV head (B)
   const int64_t* cpos;  // null, or [Hkv][ldcp] positions of the state tokens: state token
@@ -93,14 +94,15 @@ constexpr float kOPartUnscale = 1.f / 4096.f;
 // One launch: per KV head, sums the score partials (scores may be null),
 // selects the top-B or keeps all (sel); concurrently, when o_part is given
 // and S > 1, o[i] = kOPartUnscale * sum_{s<S} o_part[s*o_elems + i] in split
-// order.
+// order (o fp32, or bf16 rounded to nearest even when o_bf16).
 // Standalone mode: rt = 1 and sig_part holds the scores.  In place (ip.pos
 // set), each selection row holds the rows to refill at [0, T), the kept frame
 // tokens at [T, 2T) and their count at 2T, and the launch applies the moves;
 // app (may be null) adds the detailed-cache append to the same launch.
 hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int pool,
                          int budget, float* scores, int ldscores, int32_t* sel, int ldsel,
-                         const float* o_part, int S, int64_t o_elems, float* o, bool shared,
+                         const float* o_part, int S, int64_t o_elems, void* o, bool o_bf16,
+                         bool shared,
                          bool recent, const InPlace& ip, const AppendJob* app,
                          const Stream& st);
 

@@ -140,7 +140,7 @@ int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace, size_
   return STATEKV_OK;
 }
 
-int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const void* v, float* o,
+int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const void* v, void* o,
                           void* stream) {
   if (!L || !q || !k || !v || !o) return STATEKV_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -179,7 +179,9 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
   a.c = c;
   a.S = skv::splits_for_pool(p, pool);
   float* opart = at<float>(L, p.off_o);
-  a.o_out = a.S == 1 ? o : opart;
+  const bool out_bf16 = p.flags & STATEKV_FLAG_OUT_BF16;
+  a.o_out = a.S == 1 ? static_cast<float*>(o) : opart;  // S == 1: written as is (fp32 or bf16)
+  a.out_bf16 = out_bf16 ? 1 : 0;
 
   a.Sst = skv::stat_splits_for_pool(p, pool);
   skv::AttnArgs a1 = a;
@@ -221,7 +223,7 @@ int statekv_prefill_frame(statekv_layer* L, const void* q, const void* k, const 
       return skv::launch_select(a.sig_part, p.rt, p.ldsig, p.Hkv, pool, p.B,
                                 at<float>(L, p.off_scores), p.ldsig, at<int32_t>(L, p.off_sel),
                                 p.ldsel, a.S > 1 ? opart : nullptr, a.S,
-                                (int64_t)p.T * p.Hq * p.D, o, shared,
+                                (int64_t)p.T * p.Hq * p.D, o, out_bf16, shared,
                                 (p.flags & STATEKV_FLAG_SELECT_RECENT) != 0, ip,
                                 in_place ? &app : nullptr, ks);
     });
@@ -267,6 +269,7 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
     return STATEKV_ERR_INVALID_ARGUMENT;
   if (L->mode == 1) return STATEKV_ERR_INVALID_ARGUMENT;
   const skv::Plan& p = L->plan;
+  if (p.flags & STATEKV_FLAG_OUT_BF16) return STATEKV_ERR_INVALID_ARGUMENT;  // fp32 output only
   if (p.flags & STATEKV_FLAG_D_RING) return STATEKV_ERR_UNSUPPORTED;
   const int64_t hist = L->n * (int64_t)p.T;
   if (hist + p.T > p.cap) return STATEKV_ERR_CAPACITY;
@@ -566,7 +569,7 @@ int statekv_select_topb(const float* d_scores, int32_t n, int32_t budget, int32_
   if (n > skv::kMaxPool) return STATEKV_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(skv::launch_select(d_scores, 1, n, 1, n, budget, nullptr, 0, d_out_idx,
-                                       budget, nullptr, 1, 0, nullptr, false, false,
+                                       budget, nullptr, 1, 0, nullptr, false, false, false,
                                        skv::InPlace{}, nullptr, st));
 }
 

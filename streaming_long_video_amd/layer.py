@@ -45,7 +45,7 @@ class Layer:
         self.workspace_bytes = nbytes
 
     # -- per-frame calls -------------------------------------------------------
-    def _check_frame(self, q, k, v, out):
+    def _check_frame(self, q, k, v, out, out_dtype=torch.float32):
         T, Hq, Hkv, d = self.T, self.Hq, self.Hkv, self.d
         for name, x, shape in (("q", q, (T, Hq, d)), ("k", k, (T, Hkv, d)),
                                ("v", v, (T, Hkv, d))):
@@ -54,15 +54,17 @@ class Layer:
             if x.device != self.workspace.device:
                 raise ValueError(f"{name} is not on the layer's device")
         if out is None:
-            out = torch.empty((T, Hq, d), dtype=torch.float32, device=self.workspace.device)
-        elif (out.dtype != torch.float32 or tuple(out.shape) != (T, Hq, d)
+            out = torch.empty((T, Hq, d), dtype=out_dtype, device=self.workspace.device)
+        elif (out.dtype != out_dtype or tuple(out.shape) != (T, Hq, d)
               or not out.is_contiguous()):
-            raise ValueError("out must be a contiguous float32 tensor of shape (T, Hq, d)")
+            raise ValueError(f"out must be a contiguous {out_dtype} tensor of shape (T, Hq, d)")
         return out
 
     def prefill(self, q, k, v, out=None, stream=None):
-        """StateKV step for the next frame; returns the attention output."""
-        out = self._check_frame(q, k, v, out)
+        """StateKV step for the next frame; returns the attention output (fp32,
+        or bf16 for a layer made with STATEKV_FLAG_OUT_BF16)."""
+        bf16_out = bool(self.flags & B.STATEKV_FLAG_OUT_BF16)
+        out = self._check_frame(q, k, v, out, torch.bfloat16 if bf16_out else torch.float32)
         B.statekv_prefill_frame(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 out.data_ptr(), _stream_ptr(stream))
         return out

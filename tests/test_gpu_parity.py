@@ -330,6 +330,31 @@ def test_largest_pool(in_place):
     check_caches_bitwise(layer, ks, vs)
 
 
+@pytest.mark.parametrize("in_place,splits", [(False, 0), (True, 0), (False, 1)])
+def test_bf16_output_is_the_rounded_fp32_output(in_place, splits):
+    """STATEKV_FLAG_OUT_BF16: O as bf16 equals the fp32 output of an otherwise
+    identical layer rounded to nearest even, bit for bit, through warm-up and
+    eviction, from the split sum and (one split) from the output pass itself;
+    the state evolves identically; the quadratic baseline refuses the layer."""
+    spec = framegen.workload("tiny").replace(frame_tokens=64, state_budget=256, n_frames=6)
+    base = skv.STATEKV_FLAG_SLOT_STABLE if in_place else 0
+    a = _layer(spec, flags=base, num_splits=splits)
+    b = _layer(spec, flags=base | skv.STATEKV_FLAG_OUT_BF16, num_splits=splits)
+    qs, ks, vs = framegen.stacked_frames(spec, workers=4)
+    for n in range(spec.n_frames):
+        o32 = a.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+        o16 = b.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]))
+        assert o16.dtype == torch.bfloat16
+        assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16)), n
+    pool = spec.state_budget + spec.frame_tokens
+    assert (a.launch_plan(pool)["out_splits"] == 1) == (splits == 1)
+    sa, sb = snapshot(a), snapshot(b)
+    assert np.array_equal(sa.pos, sb.pos)
+    c = _layer(spec, flags=skv.STATEKV_FLAG_OUT_BF16)
+    with pytest.raises(skv.StateKVError):
+        c.full_attention(to_dev(qs[0]), to_dev(ks[0]), to_dev(vs[0]))
+
+
 def test_launch_plan_introspection():
     """The plan the step runs at the 8B shape: 9 output splits, 18 statistics
     splits, 7 row tiles, 68 key tiles at the full pool; at a one-frame pool

@@ -69,7 +69,12 @@ def test_workspace_bytes_and_validation():
     # in-place update: one compressed state instead of two
     m = B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_SLOT_STABLE))
     assert m <= n - 4 * 4096 * (128 * 2 * 2 + 8)
-    assert B.statekv_workspace_bytes(_cfg(flags=0b110111)) > 0  # all but C_IN_D
+    assert B.statekv_workspace_bytes(_cfg(flags=0b1110111)) > 0  # all but C_IN_D
+    # bf16 output: same workspace, and the next bit is undefined
+    assert B.statekv_workspace_bytes(_cfg(flags=B.STATEKV_FLAG_OUT_BF16)) == n
+    with pytest.raises(B.StateKVError) as e:
+        B.statekv_workspace_bytes(_cfg(flags=1 << 7))
+    assert e.value.status == -1
 
 
 def test_in_place_layout_rule():
