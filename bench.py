@@ -83,6 +83,16 @@ def useful_attention_flops(Hq, d, T, c) -> float:
     return 4.0 * Hq * d * visible_pairs(T, c)
 
 
+def gen_workers(args) -> int:
+    """Processes that generate the synthetic frames (forked from this one).
+    Under a profiler that set up the GPU before the program started, forked
+    workers inherit its state and its signal handlers, and their shutdown can
+    hang: profiled runs pass --gen-workers 1."""
+    if args.gen_workers > 0:
+        return args.gen_workers
+    return min(16, os.cpu_count() or 1)
+
+
 def gather_bytes(Hkv, d, T, B, c, rows=True) -> float:
     """C_n gather + D append, bytes that must cross HBM once.
 
@@ -187,7 +197,7 @@ def run_headline(args):
     T, Hq, Hkv, d, Bs = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
                          spec.state_budget)
     t_gen = time.perf_counter()
-    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=min(16, os.cpu_count() or 1))
+    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=gen_workers(args))
     t_gen = time.perf_counter() - t_gen
 
     dev = torch.device("cuda", 0)
@@ -333,7 +343,7 @@ def run_crossover(args):
     T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
     Ns = [32, 64, 128, 256, 512]
     Nmax = max(Ns)
-    qs, ks, vs = framegen.stacked_frames(spec, 0, Nmax, workers=min(16, os.cpu_count() or 1))
+    qs, ks, vs = framegen.stacked_frames(spec, 0, Nmax, workers=gen_workers(args))
     dev = torch.device("cuda", 0)
 
     def up(x):
@@ -401,7 +411,7 @@ def run_decode(args):
     chunk = 64
     for n0 in range(0, N, chunk):
         qs, ks, vs = framegen.stacked_frames(spec, n0, min(N, n0 + chunk),
-                                             workers=min(16, os.cpu_count() or 1))
+                                             workers=gen_workers(args))
         up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         q_d, k_d, v_d = up(qs), up(ks), up(vs)
         for i in range(q_d.shape[0]):
@@ -464,7 +474,7 @@ def run_mass(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     layer = skv.Layer(Hq, Hkv, d, T, N * T, detailed_capacity=N * T)
-    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=min(16, os.cpu_count() or 1))
+    qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=gen_workers(args))
     up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     q_d, k_d, v_d = up(qs), up(ks), up(vs)
     sets, rows = None, []
@@ -503,7 +513,7 @@ def run_depth28(args):
     layers, frames = [], []
     for l in range(L):
         s = spec.for_layer(l)
-        qs, ks, vs = framegen.stacked_frames(s, 0, N, workers=min(16, os.cpu_count() or 1))
+        qs, ks, vs = framegen.stacked_frames(s, 0, N, workers=gen_workers(args))
         up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         frames.append((up(qs), up(ks), up(vs)))
         layers.append(skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T))
@@ -540,6 +550,9 @@ def main(argv=None):
                          "launch costs a few microseconds of dispatch serialisation)")
     ap.add_argument("--breakdown-steps", type=int, default=32,
                     help="frames after the timed region with every kernel timed")
+    ap.add_argument("--gen-workers", type=int, default=0,
+                    help="processes generating the synthetic frames (0: up to 16; 1 under "
+                         "a profiler)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain device copy of this size before the timed region "
                          "(reference kernel for rocprofv3 byte counters)")
