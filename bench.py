@@ -55,7 +55,8 @@ DOMINANT = "attn_out"        # the longest kernel of the step (attention pass 2)
 def _fail_multi_gpu(n):
     print(json.dumps({"error": f"--gpus {n}: this benchmark runs on one GPU only; the "
                                "StateKV step of a layer is measured on a single MI355X "
-                               "(see the sharding notes in DESIGN.md)."}))
+                               "(per-KV-head selection shards by KV head without "
+                               "communication; layers pipeline across GPUs)."}))
     sys.exit(2)
 
 
