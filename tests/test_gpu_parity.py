@@ -125,6 +125,18 @@ def test_1b_layer_free_running_and_teacher_forced():
     assert match >= SELECT_AGREEMENT * total
 
 
+@pytest.mark.parametrize("layer_index", [0, 27])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_2b_layer_shape(layer_index, in_place):
+    """One layer of the InternVL3-2B-like 28-layer stream (Hq=12, Hkv=2, d=128,
+    B=2048, its own seed), 12 frames, the last four evicting; teacher-forced."""
+    spec = framegen.workload("internvl3_2b_28layers").for_layer(layer_index).replace(n_frames=12)
+    layer = _layer(spec, flags=skv.STATEKV_FLAG_SLOT_STABLE if in_place else 0)
+    layer, reports, (qs, ks, vs) = _run_teacher_forced(spec, layer=layer)
+    _assert_reports(reports, exact_select=False)
+    check_caches_bitwise(layer, ks, vs)
+
+
 @pytest.mark.parametrize("flags", ["c_in_d", "c_in_d_shared"])
 def test_state_kept_as_positions_into_d(flags):
     """C_IN_D: the state holds positions only and attention reads its rows
