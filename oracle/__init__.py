@@ -13,6 +13,7 @@ from .statekv_oracle import (  # noqa: F401
     frame_attention,
     full_causal_attention,
     importance_scores,
+    layer_scores,
     rope_at_positions,
     round_to_bf16,
     select_most_recent,

@@ -101,6 +101,20 @@ def importance_scores(P_heads: List[np.ndarray]) -> np.ndarray:
     return sigma
 
 
+def layer_scores(per_head_scores: List[np.ndarray]) -> np.ndarray:
+    """Importance for the layer-wide (SHARED) selection: the per-KV-head scores
+    of one pool summed over every KV head, i.e. the sum over every query head
+    of the layer and every frame query (reading of rainbus method steps, which
+    defines importance as a sum over queries without fixing the heads; the
+    default instead keeps one set per KV head, paperlayer App. A "Protocol").
+    Every head's pool holds the same positions in the same order, so the
+    entries align."""
+    total = np.zeros_like(np.asarray(per_head_scores[0], dtype=np.float64))
+    for s in per_head_scores:
+        total = total + np.asarray(s, dtype=np.float64)
+    return total
+
+
 def select_top_b(scores: np.ndarray, positions: np.ndarray, budget: int) -> np.ndarray:
     """Indices (into the pool) of the top-``budget`` candidates, ascending position.
 
@@ -256,8 +270,7 @@ class StateKVOracle:
 
         # the compressed state becomes the top-B of the pool
         if self.shared:
-            total = np.sum(scores, axis=0)
-            keep_shared = select_top_b(total, pools[0], self.B)
+            keep_shared = select_top_b(layer_scores(scores), pools[0], self.B)
         kept = []
         for h in range(Hkv):
             if self.recency:

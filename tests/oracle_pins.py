@@ -323,6 +323,66 @@ def check_attention_mass() -> None:
         assert not len(outside) or inside.min() >= outside.max()
 
 
+def check_shared_layer_ranking() -> None:
+    """SHARED selection with two KV heads, worked by hand.
+
+    Hq = Hkv = 2 (G = 1), d = 1, T = 3, B = 2, softmax scale ln 2 and every
+    query q = 1, so the weight of key j is 2^k_j / (sum over visible keys).
+    Keys [0, 0, 3] give importance [8/5, 3/5, 4/5] (query 2 weights the frame
+    1:1:8); keys [0, 0, 1] give [7/4, 3/4, 1/2] (query 2 weights 1:1:2).  Per
+    KV head the first keeps positions {0, 2}, the second {0, 1}; the layer sum
+    [67/20, 27/20, 13/10] keeps {0, 1} for both heads, while either head alone
+    or the head-wise maximum ([7/4, 3/4, 4/5]) would keep {0, 2} in one of the
+    two head orders.  (rainbus method steps: importance is a sum over queries;
+    the layer-wide set sums every query head of the layer.)"""
+    a = [Fraction(8, 5), Fraction(3, 5), Fraction(4, 5)]
+    b = [Fraction(7, 4), Fraction(3, 4), Fraction(1, 2)]
+    for keys, want in (([[0, 0, 3], [0, 0, 1]], [a, b]), ([[0, 0, 1], [0, 0, 3]], [b, a])):
+        q = np.ones((3, 2, 1))
+        k = np.array(keys, dtype=np.float64).T[:, :, None]      # (T, Hkv, 1)
+        v = np.arange(6, dtype=np.float64).reshape(3, 2, 1)
+        per = so.StateKVOracle(2, 2, 1, 3, 2, scale=math.log(2.0))
+        lay = so.StateKVOracle(2, 2, 1, 3, 2, scale=math.log(2.0), shared=True)
+        rp, rl = per.step(q, k, v), lay.step(q, k, v)
+        for h in range(2):
+            np.testing.assert_allclose(rl.scores[h], [float(x) for x in want[h]], rtol=0,
+                                       atol=1e-14)
+            np.testing.assert_array_equal(rl.kept_positions[h], [0, 1])
+            np.testing.assert_array_equal(rl.o[:, h], rp.o[:, h])
+        np.testing.assert_array_equal(rp.kept_positions[keys.index([0, 0, 3])], [0, 2])
+        np.testing.assert_array_equal(rp.kept_positions[keys.index([0, 0, 1])], [0, 1])
+
+
+def check_noncausal_closed_form() -> None:
+    """Frame tokens visible to every frame query (the non-causal variant), all
+    keys zero: every query sees the whole pool [C ; frame] with equal weight,
+    so O_t is the mean of the pool's values for every t and every candidate's
+    importance is G*T/(c+T); with all importances tied the lower positions are
+    kept, so the state holds positions 0..B-1 once it is full."""
+    rng = np.random.default_rng(13)
+    Hq, Hkv, d, T, B = 6, 2, 4, 5, 7
+    G = Hq // Hkv
+    orc = so.StateKVOracle(Hq, Hkv, d, T, B, causal=False)
+    for n in range(3):
+        q = rng.standard_normal((T, Hq, d))
+        k = np.zeros((T, Hkv, d))
+        v = rng.standard_normal((T, Hkv, d))
+        prev = [orc.state(h) for h in range(Hkv)]
+        prev = [(p.copy(), None if vv is None else vv.copy()) for p, _, vv in prev]
+        res = orc.step(q, k, v)
+        for h in range(Hkv):
+            c = prev[h][0].shape[0]
+            pool_v = v[:, h, :] if c == 0 else np.concatenate([prev[h][1], v[:, h, :]])
+            for t in range(T):
+                for g in range(h * G, (h + 1) * G):
+                    np.testing.assert_allclose(res.o[t, g], pool_v.mean(axis=0), rtol=0,
+                                               atol=1e-13)
+            np.testing.assert_allclose(res.scores[h], np.full(c + T, G * T / (c + T)),
+                                       rtol=0, atol=1e-13)
+            np.testing.assert_array_equal(res.kept_positions[h],
+                                          np.arange(min(B, (n + 1) * T)))
+
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -335,4 +395,6 @@ ALL_CHECKS = [
     check_rope_and_rounding,
     check_recency_window,
     check_attention_mass,
+    check_shared_layer_ranking,
+    check_noncausal_closed_form,
 ]

@@ -13,6 +13,7 @@ import oracle_pins
 _orig_attention = so.frame_attention
 _orig_scores = so.importance_scores
 _orig_select = so.select_top_b
+_orig_layer = so.layer_scores
 
 
 def attention_causal_off_by_one(q, keys, values, n_state, scale, causal=True):
@@ -76,6 +77,22 @@ def select_off_by_one_budget(scores, positions, budget):
     return _orig_select(scores, positions, max(1, budget - 1))
 
 
+def attention_causal_always(q, keys, values, n_state, scale, causal=True):
+    return _orig_attention(q, keys, values, n_state, scale, True)
+
+
+def layer_first_head_only(per_head_scores):
+    return np.asarray(per_head_scores[0], dtype=np.float64)
+
+
+def layer_last_head_only(per_head_scores):
+    return np.asarray(per_head_scores[-1], dtype=np.float64)
+
+
+def layer_headwise_max(per_head_scores):
+    return np.max(np.asarray(per_head_scores, dtype=np.float64), axis=0)
+
+
 MUTANTS = [
     ("frame_attention", attention_causal_off_by_one),
     ("frame_attention", attention_mask_on_state_too),
@@ -87,6 +104,10 @@ MUTANTS = [
     ("select_top_b", select_ties_to_higher_position),
     ("select_top_b", select_smallest_scores),
     ("select_top_b", select_off_by_one_budget),
+    ("frame_attention", attention_causal_always),
+    ("layer_scores", layer_first_head_only),
+    ("layer_scores", layer_last_head_only),
+    ("layer_scores", layer_headwise_max),
 ]
 
 
