@@ -6,18 +6,23 @@ One step = one frame through one layer: attention over [C_{n-1} ; frame]
 with importance scores, top-B select, the state update C_n and the append to
 D (every row of the hot path).  By default C is updated in place (kept rows
 stay, kept frame tokens fill the freed rows; --state-layout rows rewrites C_n
-in position order with a separate gather launch).  Default workload: the InternVL3-8B-like layer
-(Hq=28, Hkv=4, d=128, T=256, B=4096), W=16 warm-up frames (they fill the
-state: 16*256 = B) and K=496 timed frames, i.e. the pages' 512-frame stream.
-All frames are generated on the host (seeded, synthetic) and staged in HBM
-before the timed region.
+in position order with a separate gather launch).  Default workload: the
+InternVL3-8B-like layer (Hq=28, Hkv=4, d=128, T=256, B=4096) over the pages'
+512-frame stream, D preallocated for all of it (131072 tokens).  The first
+ceil(B/T) = 16 frames fill the state (no eviction, smaller pools) and are
+never timed; then W more untimed frames, then K timed frames, every one at
+the full pool of B + T = 4352 candidates (defaults: W=0, K=496, i.e. frames
+16..511).  All frames are generated on the host (seeded, synthetic) and
+staged in HBM before the timed region.
 
 Prints ONE JSON line: frames/s per layer over the K timed frames (no
-per-launch instrumentation inside them), a roofline entry for the dominant
-kernel and the per-kernel breakdown (launch durations from HIP events that the
-dispatch itself timestamps on the launch stream, over the 32 frames right
-after the timed region, state still full), and the float64 CPU oracle timed
-on a bounded sample of the same stream.
+per-launch instrumentation inside them); the per-kernel breakdown (launch
+durations from HIP events that the dispatch itself timestamps on the launch
+stream) over the 32 frames right after the timed region, and the per-frame
+distribution (median, p5, p95) over the 64 frames after those, all at the
+same pool size; a roofline entry for the dominant kernel whose flops are
+those of that pool; the state update's algorithmic HBM rate; and the float64
+CPU oracle timed on a bounded sample of the same stream.
 
 Other measurements (not the headline line):
     --mode crossover   StateKV vs quadratic full attention, 1B shape,
@@ -85,10 +90,9 @@ def useful_attention_flops(Hq, d, T, c) -> float:
 
 
 def gen_workers(args) -> int:
-    """Processes that generate the synthetic frames (forked from this one).
-    Under a profiler that set up the GPU before the program started, forked
-    workers inherit its state and its signal handlers, and their shutdown can
-    hang: profiled runs pass --gen-workers 1."""
+    """Processes that generate the synthetic frames (spawned, so nothing this
+    process has set up on the GPU is inherited; profiled runs still pass
+    --gen-workers 1 to keep the profiler's process tree small)."""
     if args.gen_workers > 0:
         return args.gen_workers
     return min(16, os.cpu_count() or 1)
@@ -108,28 +112,56 @@ def gather_bytes(Hkv, d, T, B, c, rows=True) -> float:
     return float(gather + append)
 
 
-def select_bytes(Hkv, Hq, d, T, B, c, plan, in_place) -> float:
-    """The select launch's bytes that must cross HBM once (state moves excluded:
-    at most Hkv*T rows, data-dependent).
+def state_update_bytes(Hkv, d, T, B, moved_rows, in_place) -> float:
+    """Algorithmic bytes of the state update (select, C_n, D append) at the
+    steady state, as the scope table counts them: read the pool's importance
+    (Hkv*(B+T) floats); write the selection (kept indices, or in place the
+    move lists of 2T+1 words per head); move the kept rows (in place only the
+    kept frame tokens: read and write their K and V rows; with the rewritten
+    state every kept row plus its position); append the frame to D (read and
+    write its K and V rows).  Split partials (score row tiles, O splits) are
+    the attention's implementation traffic and are reported separately."""
+    row = 2 * d * 2
+    sigma = Hkv * (B + T) * 4
+    sel = Hkv * ((2 * T + 1) if in_place else B) * 4
+    if in_place:
+        moves = moved_rows * 2 * row
+    else:
+        moves = Hkv * B * (2 * row + 8 + 8 + 4)
+    append = Hkv * T * 2 * row
+    return float(sigma + sel + moves + append)
 
-    Read the row tiles' score partials and write the scores; write the
-    selection (kept indices, or in place the move lists); when the output pass
-    ran in several key splits, read their O partials and write O; in place,
-    also the D append (read the frame's K and V rows, write them to D)."""
-    pool = c + T
-    scores = Hkv * plan["row_tiles"] * pool * 4 + Hkv * pool * 4
-    sel = Hkv * (2 * T + 1 if in_place else min(B, pool)) * 4
+
+def split_partial_bytes(Hq, Hkv, d, T, plan) -> dict:
+    """Bytes the split-K attention writes and reads back beyond the algorithm:
+    per-split row statistics, per-row-tile score partials, per-split O."""
+    stat = plan["stat_splits"] * Hq * T * 2 * 4
+    pool_words = plan["key_tiles"] * 64
+    score = Hkv * plan["row_tiles"] * pool_words * 4
     S = plan["out_splits"]
-    osum = (S + 1) * T * Hq * d * 4 if S > 1 else 0
-    append = Hkv * T * 2 * (2 * d * 2) if in_place else 0
-    return float(scores + sel + osum + append)
+    opart = S * T * Hq * d * 4 if S > 1 else 0
+    return {"stat_partials_written": float(stat), "score_partials_written": float(score),
+            "o_partials_written": float(opart)}
 
 
 # ----------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on host cores
 # ----------------------------------------------------------------------------
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(spec, qs, ks, vs, warm: int, budget_s: float):
+    """The oracle as it stands, one process, numpy's BLAS threads, on a bounded
+    sample of the same stream (frames after the state has filled)."""
     from threadpoolctl import threadpool_info
 
     from oracle import StateKVOracle
@@ -146,15 +178,22 @@ def cpu_baseline(spec, qs, ks, vs, warm: int, budget_s: float):
         n += 1
         done += 1
     dt = time.perf_counter() - t0
-    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
     return {
         "value": done / dt,
         "unit": "frames/s per layer",
-        "cores": int(max(blas) if blas else 1),
+        "cores": int(threads),
         "host_cores": len(os.sched_getaffinity(0)),
+        "processes": 1,
+        "cpu_model": _cpu_model(),
+        "numpy": np.__version__,
+        "blas": [{"library": p.get("internal_api"), "version": p.get("version"),
+                  "threads": p.get("num_threads")} for p in blas],
         "kind": "oracle",
         "sample": (f"float64 numpy oracle, frames {warm}..{warm + done - 1} of the same "
-                   f"stream after it ran frames 0..{warm - 1} untimed; {dt:.1f} s"),
+                   f"stream (state full) after it ran frames 0..{warm - 1} untimed; "
+                   f"{dt:.1f} s in one process"),
     }
 
 
@@ -183,6 +222,10 @@ def measured_traffic(kernel: str):
 # headline: one layer, 512-frame stream
 # ----------------------------------------------------------------------------
 
+def _pct(x, q):
+    return float(np.percentile(np.asarray(x, dtype=np.float64), q))
+
+
 def run_headline(args):
     import torch
 
@@ -192,11 +235,16 @@ def run_headline(args):
     spec = framegen.workload(args.workload)
     if spec.n_layers != 1:
         raise SystemExit("the headline mode runs single-layer workloads")
-    W, K = args.warmup, args.steps
-    KB = args.breakdown_steps  # extra frames after the timed region, every kernel timed
-    N = W + K + KB
     T, Hq, Hkv, d, Bs = (spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim,
                          spec.state_budget)
+    # frames 0..fill-1 fill the state (c < B, no eviction): never timed
+    fill = -(-Bs // T)
+    W, K = args.warmup, args.steps
+    KB = args.breakdown_steps  # every kernel timed with HIP events
+    KD = args.dist_steps       # one HIP event per frame boundary
+    first = fill + W           # first timed frame
+    N = first + K + KB + KD
+    cap_frames = max(spec.n_frames, N)  # D sized for the whole stream
     t_gen = time.perf_counter()
     qs, ks, vs = framegen.stacked_frames(spec, 0, N, workers=gen_workers(args))
     t_gen = time.perf_counter() - t_gen
@@ -212,10 +260,11 @@ def run_headline(args):
              "inplace": skv.STATEKV_FLAG_SLOT_STABLE,
              "inplace-positions": skv.STATEKV_FLAG_SLOT_STABLE | skv.STATEKV_FLAG_C_IN_D,
              }[args.state_layout]
-    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T, num_splits=args.splits,
-                      flags=flags)
+    in_place = args.state_layout.startswith("inplace")
+    layer = skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=cap_frames * T,
+                      num_splits=args.splits, flags=flags)
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
-    for n in range(W):
+    for n in range(first):
         layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
     if args.copy_probe_mib > 0:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
@@ -227,6 +276,10 @@ def run_headline(args):
             torch.neg(src, out=dst)
         del src, dst
     torch.cuda.synchronize()
+    c_steady = layer.state()["count"]
+    if c_steady != Bs:
+        raise SystemExit(f"state not full before the timed region ({c_steady} of {Bs})")
+    pool = c_steady + T
 
     all_mask = (1 << len(skv.STATEKV_KERNELS)) - 1
     mask = {"none": 0, "dominant": 1 << skv.STATEKV_KERNELS.index(DOMINANT),
@@ -235,28 +288,48 @@ def run_headline(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        layer.prefill(q_all[W + i], k_all[W + i], v_all[W + i], out=out)
+        layer.prefill(q_all[first + i], k_all[first + i], v_all[first + i], out=out)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     prof = skv.statekv_profile_stop(layer.handle)
-
-    # per-kernel breakdown on the frames after the timed region (events around
-    # every launch cost a little time, so they stay out of the timed frames)
     kernels_us = {k: (ms / cnt * 1e3 if cnt else None) for k, (ms, cnt) in prof.items()}
+
+    # per-kernel launch durations on the frames right after the timed region
+    # (events around every launch cost a little time, so they stay out of it);
+    # every one of these frames runs at the same pool size as the timed ones
+    n0 = first + K
+    breakdown_us = {}
+    moved_rows = None
     if KB > 0:
         skv.statekv_profile_start(layer.handle, all_mask, KB * len(skv.STATEKV_KERNELS))
         for i in range(KB):
-            n = W + K + i
-            layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+            layer.prefill(q_all[n0 + i], k_all[n0 + i], v_all[n0 + i], out=out)
         torch.cuda.synchronize()
         bd = skv.statekv_profile_stop(layer.handle)
         breakdown_us = {k: ms / cnt * 1e3 for k, (ms, cnt) in bd.items() if cnt}
-    else:
-        breakdown_us = {k: v for k, v in kernels_us.items() if v}
+        # rows the last of these frames moved: its kept frame tokens, all heads
+        st = layer.state()
+        last0 = (n0 + KB - 1) * T + layer.position_offset
+        moved_rows = int((st["pos"][:, :st["count"]] >= last0).sum().item())
+    # per-frame wall time distribution: one event per frame boundary
+    n1 = n0 + KB
+    frame_us = None
+    if KD > 0:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(KD + 1)]
+        ev[0].record()
+        for i in range(KD):
+            layer.prefill(q_all[n1 + i], k_all[n1 + i], v_all[n1 + i], out=out)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(KD)]
+        frame_us = {"mean": float(np.mean(per)), "median": _pct(per, 50),
+                    "p5": _pct(per, 5), "p95": _pct(per, 95),
+                    "frames": f"{n1}..{n1 + KD - 1}",
+                    "how": "HIP events recorded between consecutive frames on the launch stream"}
+    if layer.state()["pool"] != pool:
+        raise SystemExit("the pool size changed during the measured frames")
 
-    cs = [min(Bs, n * T) for n in range(W, W + K)]
-    dominant = DOMINANT
-    flops = float(np.mean([attn_out_flops(Hq, d, T, c) for c in cs]))
+    plan = layer.launch_plan(pool)
     result = {
         "metric": "video-prefill frames/s per layer + % bf16 MFMA peak (8B shape, B=4096, T=256)",
         "value": K / elapsed,
@@ -274,14 +347,21 @@ def run_headline(args):
         "config": {"workload": args.workload, "state_layout": args.state_layout,
                    "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": d, "frame_tokens": T, "state_budget": Bs,
-                   "frames": N, "detailed_capacity": N * T},
+                   "stream_frames": spec.n_frames, "frames_run": N,
+                   "detailed_capacity": cap_frames * T,
+                   "fill_frames_untimed": fill, "timed_frames": f"{first}..{first + K - 1}",
+                   "timed_pool": pool},
     }
-    # the dominant kernel's launch duration: HIP events timestamped by the
-    # dispatch on the launch stream -- from the timed region when it was
-    # instrumented, else from the breakdown frames that follow it
+    if frame_us:
+        result["per_frame_us"] = frame_us
+    # the dominant kernel: its algorithmic flops at the pool of the frames whose
+    # launch durations are used (HIP events the dispatch itself timestamps on
+    # the launch stream): the timed region when it was instrumented, else the
+    # breakdown frames that follow it
+    flops = attn_out_flops(Hq, d, T, c_steady)
     att = kernels_us.get("attn_out") or breakdown_us.get("attn_out")
     att_src = ("timed region" if kernels_us.get("attn_out") else
-               f"frames {W + K}..{W + K + KB - 1}, right after the timed region")
+               f"frames {n0}..{n0 + KB - 1}, right after the timed region")
     if att:
         achieved = flops / (att * 1e-6) / 1e12
         result["roofline"] = {
@@ -289,44 +369,38 @@ def run_headline(args):
             "bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_TFLOPS,
             "traffic": measured_traffic("attn_out"),
-            "flops_per_launch": flops, "avg_launch_us": att,
+            "flops_per_launch": flops, "pool": pool, "avg_launch_us": att,
             "avg_launch_us_from": "HIP events on the launch stream, " + att_src,
         }
     if breakdown_us.get("attn_stats") and breakdown_us.get("attn_out"):
-        useful = float(np.mean([useful_attention_flops(Hq, d, T, c) for c in cs]))
+        useful = useful_attention_flops(Hq, d, T, c_steady)
         t_att = (breakdown_us["attn_stats"] + breakdown_us["attn_out"]) * 1e-6
         result["attention"] = {
+            "useful_gflop": useful / 1e9,
             "useful_tflops": useful / t_att / 1e12,
             "useful_frac_of_peak": useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
             "executed_frac_of_peak": 1.5 * useful / t_att / 1e12 / PEAK_MFMA_TFLOPS,
         }
-    if breakdown_us.get("gather"):
-        gb = float(np.mean([gather_bytes(Hkv, d, T, Bs, c, rows=args.state_layout == "rows")
-                            for c in cs]))
-        tg = breakdown_us["gather"]
-        result["gather_append"] = {
-            "bytes_per_launch": gb, "avg_launch_us": tg,
-            "achieved_gbs": gb / (tg * 1e-6) / 1e9,
-            "frac_of_hbm_peak": gb / (tg * 1e-6) / 1e9 / PEAK_HBM_GBS,
+    upd_us = (breakdown_us.get("select") or 0.0) + (breakdown_us.get("gather") or 0.0)
+    if upd_us and moved_rows is not None:
+        ub = state_update_bytes(Hkv, d, T, Bs, moved_rows, in_place)
+        result["state_update"] = {
+            "launches": ["select"] + ([] if in_place else ["gather"]),
+            "algorithmic_bytes": ub, "us": upd_us,
+            "achieved_gbs": ub / (upd_us * 1e-6) / 1e9,
+            "frac_of_hbm_peak": ub / (upd_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "moved_rows_last_frame": moved_rows,
+            "counts": "importance read, selection written, kept rows moved, D append "
+                      "(read + write); not the attention's split partials",
         }
-    if breakdown_us.get("select"):
-        in_place = args.state_layout.startswith("inplace")
-        sb = float(np.mean([select_bytes(Hkv, Hq, d, T, Bs, c, layer.launch_plan(c + T), in_place)
-                            for c in cs]))
-        ts = breakdown_us["select"]
-        result["select_launch"] = {
-            "bytes_per_launch": sb, "avg_launch_us": ts,
-            "achieved_gbs": sb / (ts * 1e-6) / 1e9,
-            "frac_of_hbm_peak": sb / (ts * 1e-6) / 1e9 / PEAK_HBM_GBS,
-            "includes": "score sums, selection, O split sum" + (", D append" if in_place else ""),
-        }
+    result["split_partials"] = dict(split_partial_bytes(Hq, Hkv, d, T, plan), plan=plan)
     result["kernels_us"] = {k: v for k, v in breakdown_us.items()}
-    result["kernels_us_frames"] = f"{W + K}..{W + K + KB - 1}" if KB > 0 else "timed frames"
-    result["dominant_kernel"] = dominant
+    result["kernels_us_frames"] = f"{n0}..{n0 + KB - 1}" if KB > 0 else None
+    result["dominant_kernel"] = DOMINANT
     result["event_mode"] = args.events
     result["input_generation_s"] = t_gen
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, qs, ks, vs, W, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(spec, qs, ks, vs, fill, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -539,8 +613,10 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=496)
-    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=496,
+                    help="timed frames (all at the full state)")
+    ap.add_argument("--warmup", type=int, default=0,
+                    help="untimed frames after the state-fill frames (ceil(B/T), never timed)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode", "mass"],
                     default="headline")
@@ -551,6 +627,8 @@ def main(argv=None):
                          "launch costs a few microseconds of dispatch serialisation)")
     ap.add_argument("--breakdown-steps", type=int, default=32,
                     help="frames after the timed region with every kernel timed")
+    ap.add_argument("--dist-steps", type=int, default=64,
+                    help="frames after those with one event per frame (median, p5, p95)")
     ap.add_argument("--gen-workers", type=int, default=0,
                     help="processes generating the synthetic frames (0: up to 16; 1 under "
                          "a profiler)")

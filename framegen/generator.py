@@ -259,7 +259,9 @@ def stacked_frames(spec: FrameSpec, start: int = 0, stop: Optional[int] = None,
     jobs = [(spec, i) for i in range(start, stop)]
     if workers > 1 and n > 1:
         import multiprocessing as mp
-        with mp.get_context("fork").Pool(min(workers, n)) as pool:
+        # spawned, never forked: a caller that already initialised the GPU
+        # (or runs under a profiler that did) must not hand its state down
+        with mp.get_context("spawn").Pool(min(workers, n)) as pool:
             for i, (a, b, c) in enumerate(pool.imap(_frame_job, jobs, chunksize=4)):
                 q[i], k[i], v[i] = a, b, c
     else:

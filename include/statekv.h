@@ -28,6 +28,11 @@
  *     original positions p = position_offset + n*T + t.  The library never
  *     applies positional encoding; it only records p.
  *   - O is written as float32 [T][Hq][d].
+ *   - Numeric preconditions (not checked; violating them gives inf/NaN in O,
+ *     never a fault): q, k and v are finite, and |v| < 65504 -- the value
+ *     side of the attention runs on fp16 matrix instructions, which hold
+ *     every bf16 value of that range (exactly for |v| >= 2^-17).  NaN or inf
+ *     inputs give an unspecified selection (never an out-of-range index).
  *   - `stream` is a hipStream_t (NULL = default stream).  Work is enqueued
  *     asynchronously; results are ready once the stream is synchronised.
  *   - The caller owns every device buffer, including the one workspace; the
@@ -175,18 +180,23 @@ int statekv_workspace_bytes(const statekv_layer_config* cfg, size_t* bytes);
 int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace,
                        size_t workspace_bytes, statekv_layer** out);
 
-/* The per-frame StateKV step (the four parts listed at the top) for the next
- * frame n = frames_seen: reads q/k/v, writes o, updates C and D, and advances
- * frames_seen.  Kernels: attention statistics pass, attention output + score
+/* The per-frame StateKV step (the four parts listed at the top; rainbus
+ * method steps; paperlayer section 3.3) for the next frame n = frames_seen:
+ * reads q/k/v, writes o, updates C and D, and advances frames_seen.  The
+ * numeric preconditions above apply (finite inputs, |v| < 65504).  Kernels: attention statistics pass, attention output + score
  * pass, top-B select (with the split-O reduction in the same launch),
  * gather + detailed-cache append (with SLOT_STABLE the select launch applies
  * the state update and the append itself: three launches). */
 int statekv_prefill_frame(statekv_layer* layer, const void* q, const void* k,
                           const void* v, void* o, void* stream);
 
-/* Quadratic baseline on the same layer object (full causal self-attention, the
- * pages' "Full SA"): appends the frame to D, then the frame's queries attend
- * over D[0 : (n+1)T] causally; C is never touched.  A layer serves either this
+/* Quadratic baseline on the same layer object: full causal self-attention
+ * ("Full SA"), in which every position attends to every earlier position, so
+ * frame n costs O(nT^2) and a video O((TN)^2) (rainbus prerequisites, section
+ * on self-attention complexity; paperlayer App. C.1-C.2 compare StateKV's
+ * marginal and cumulative compute against it).  Appends the frame to D, then
+ * the frame's queries attend over D[0 : (n+1)T] causally; C is never
+ * touched.  Same numeric preconditions as statekv_prefill_frame.  A layer serves either this
  * or statekv_prefill_frame, not both (mixing returns INVALID_ARGUMENT).  Needs
  * a linear (non-ring) D. */
 int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void* k,
@@ -207,7 +217,8 @@ int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void
  *   frames_seen >= 1 (else STATEKV_ERR_INVALID_ARGUMENT).
  * Works after statekv_prefill_frame or statekv_full_attention_frame and
  * changes no layer state; uses the workspace's split-partial regions, so it
- * must not overlap a prefill call of the same layer.  Kernels: DECODE (one
+ * must not overlap a prefill call of the same layer.  Same numeric
+ * preconditions as statekv_prefill_frame (finite q and D, |v| < 65504).  Kernels: DECODE (one
  * wave per KV head and D split), then SPLIT_SUM (split combine). */
 int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_queries, float* o,
                              void* stream);
@@ -221,7 +232,19 @@ int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_quer
 int statekv_rope(statekv_layer* layer, void* x, int32_t n_tokens, int32_t n_heads,
                  int64_t first_position, void* stream);
 
-/* Views (host only). */
+/* Views (host only; they enqueue nothing and never fail on a valid layer;
+ * STATEKV_ERR_INVALID_ARGUMENT for a null argument).
+ * statekv_state: the compressed state C_n, the fixed-capacity, importance-
+ * selected temporal state that only the streaming prefill reads (rainbus
+ * method steps: a compressed state of capacity B per layer; rainbus
+ * technical novelty: this cache serves the video prefill only), plus the
+ * importance of each candidate of the last frame's pool (the ranking that
+ * chose C_n).
+ * statekv_detailed_cache: the detailed state D_n, every visual token of every
+ * frame so far, kept for the final text decoding (rainbus method steps: the
+ * detailed state accumulates all visual tokens up to frame n; rainbus core
+ * method and gist.science/nl "Het Proces": decoding runs over all video
+ * tokens). */
 int statekv_state(const statekv_layer* layer, statekv_state_view* out);
 int statekv_detailed_cache(const statekv_layer* layer, statekv_cache_view* out);
 
@@ -319,8 +342,11 @@ enum {
 int statekv_profile_start(statekv_layer* layer, uint32_t kernel_mask, int32_t max_records);
 int statekv_profile_stop(statekv_layer* layer, double* total_ms, int64_t* launches);
 
-/* The top-B select used inside the step, exposed for bit-exact testing: of the
- * n fp32 scores (device, non-negative or +0; NaN ranks lowest), keep
+/* The top-B select used inside the step (rainbus method steps and paperlayer
+ * section 3.3: C_n = the B candidates of C_{n-1} plus the frame with the
+ * largest summed attention weight; ties to the lower position are this
+ * library's reading, the pages leave ties open), exposed for bit-exact
+ * testing: of the n fp32 scores (device, non-negative or +0; NaN ranks lowest), keep
  * min(budget, n) indices -- larger score first, ties to the lower index -- and
  * write them in ascending index order to d_out_idx (device, >= min(budget,n)
  * int32).  1 <= n <= 32768, budget >= 1. */

@@ -45,6 +45,12 @@ KERNELS = {
 PROBE = r"neg"  # torch's negation kernel: the copy probe
 
 SOURCES = (
+    # the host plan and launch code choose split counts and grids, which
+    # decide part of the measured traffic
+    "csrc/plan.h",
+    "csrc/plan.cpp",
+    "csrc/skv_internal.h",
+    "csrc/statekv_api.hip",
     "csrc/kernels/attention.hip",
     "csrc/kernels/select.hip",
     "csrc/kernels/gather.hip",
@@ -54,7 +60,8 @@ SOURCES = (
 
 
 def source_hash() -> str:
-    """Hash of the kernel sources: counters taken on other sources are stale."""
+    """Hash of the kernel and launch-plan sources: counters taken on other
+    sources are stale."""
     here = os.path.dirname(os.path.abspath(__file__))
     h = hashlib.sha256()
     for rel in SOURCES:

@@ -15,9 +15,13 @@ from oracle import select_most_recent, select_top_b
 # oracle, both fed identical bf16 inputs).
 O_MAXABS = 2e-2
 O_RELRMS = 1e-3
-# fp32 scores against float64 scores
-SCORE_RTOL = 2e-4
-SCORE_ATOL = 2e-5
+# fp32 scores against float64 scores: each probability carries ~1e-6
+# relative error (fp32 logits from bf16 products, the exp2 instruction, the
+# row log-sum-exp) and the fixed-order fp32 sums over <= 1792 positive terms
+# add about as much; the bound sits ~10x above that (observed max about
+# 0.04 of it at the 8B shape)
+SCORE_RTOL = 1e-5
+SCORE_ATOL = 1e-6
 # free-running selected-set agreement
 SELECT_AGREEMENT = 0.995
 
