@@ -2,8 +2,10 @@
 B=4096, 512 frames, D preallocated for 131072 tokens), in the launch
 configuration the benchmark times (the in-place state update) and with the
 position-ordered gather.  The oracle checks sampled frames one by
-one from the GPU's own state (teacher forced); properties that hold at any
-size are checked on every frame."""
+one from the GPU's own state (teacher forced); the GPU's free-running kept
+sets are compared with the free-running oracle's (stored by
+tests/golden/make_sink_survival.py) at six frames, at least 99.5 % agreement;
+properties that hold at any size are checked on every frame."""
 
 import json
 import os
@@ -12,8 +14,9 @@ import numpy as np
 import pytest
 
 import framegen
-from gpu_util import (O_MAXABS, O_RELRMS, check_caches_bitwise, snapshot, teacher_forced_frame,
-                      to_dev)
+from gpu_util import (O_MAXABS, O_RELRMS, SELECT_AGREEMENT, check_caches_bitwise, snapshot,
+                      teacher_forced_frame, to_dev)
+from golden.make_sink_survival import decode_set
 from oracle import StateKVOracle
 
 pytestmark = pytest.mark.gpu
@@ -27,6 +30,7 @@ import streaming_long_video_amd as skv  # noqa: E402
 SAMPLED = {0, 15, 16, 17, 100, 301, 511}
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                       "sink_survival_8b.json")
+KEPT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "kept_sets_8b.json")
 
 
 def _oracle_sinks_kept(golden, h, n, T):
@@ -54,6 +58,10 @@ def test_8b_layer_512_frames(frames_8b, layout):
     _, sinks = framegen.sink_plan(spec)
     golden = json.load(open(GOLDEN))
     assert golden["sink_positions"] == [int(x) for x in sinks]
+    # the free-running oracle's whole kept sets at a few frames (the GPU runs
+    # free too: the teacher-forced frames below only read its state)
+    kept_golden = json.load(open(KEPT))["frames"]
+    agree = {}
     G, T = spec.group, spec.frame_tokens
     out = torch.empty((T, spec.n_q_heads, spec.head_dim), dtype=torch.float32, device="cuda")
     worst = (0.0, 0.0)
@@ -68,6 +76,15 @@ def test_8b_layer_512_frames(frames_8b, layout):
             worst = max(worst, (r.relrms, r.maxabs))
         else:
             layer.prefill(to_dev(qs[n]), to_dev(ks[n]), to_dev(vs[n]), out=out)
+        if str(n) in kept_golden:
+            snap = snapshot(layer)
+            hits = total = 0
+            for h in range(spec.n_kv_heads):
+                ref = decode_set(kept_golden[str(n)][str(h)], (n + 1) * T)
+                hits += int(np.isin(snap.pos[h], ref).sum())
+                total += ref.shape[0]
+            agree[n] = (hits, total)
+            print(f"frame {n}: free-running kept-set agreement {hits}/{total}")
         if n % 8 == 7 or n in SAMPLED:
             snap = snapshot(layer)
             assert snap.count == min(spec.state_budget, (n + 1) * T)
@@ -81,3 +98,10 @@ def test_8b_layer_512_frames(frames_8b, layout):
                 assert held == _oracle_sinks_kept(golden, h, n, T), (n, h)
     check_caches_bitwise(layer, ks, vs)
     print(f"worst sampled relrms {worst[0]:.3e}")
+    # acceptance: selected-set agreement with the free-running oracle
+    assert sorted(agree) == sorted(int(x) for x in kept_golden)
+    hits = sum(a for a, _ in agree.values())
+    total = sum(b for _, b in agree.values())
+    worst_frame = min(a / b for a, b in agree.values())
+    print(f"free-running agreement {hits / total:.5f} (worst sampled frame {worst_frame:.5f})")
+    assert hits >= SELECT_AGREEMENT * total, agree
