@@ -11,9 +11,11 @@ from .statekv_oracle import (  # noqa: F401
     decode_attention,
     decode_bf16,
     frame_attention,
+    frame_front_end,
     full_causal_attention,
     importance_scores,
     layer_scores,
+    project_frame,
     rope_at_positions,
     round_to_bf16,
     select_most_recent,

@@ -390,6 +390,35 @@ def rope_at_positions(x, positions, theta: float, scaling: float = 1.0) -> np.nd
     return np.concatenate([z.real, z.imag], axis=-1)
 
 
+def project_frame(x, w_q, w_k, w_v, n_q_heads: int, n_kv_heads: int, head_dim: int):
+    """The frame's queries, keys and values from its visual-token hidden states.
+
+    rainbus summary, method steps: for frame n, Q_n = X_n W_Q, K_n = X_n W_K,
+    V_n = X_n W_V, where X_n holds the hidden states of the frame's visual
+    tokens.  x: (T, hidden); w_q: (hidden, Hq*d); w_k, w_v: (hidden, Hkv*d)
+    (bf16 bits or floats).  Output columns h*d .. h*d+d-1 form head h.  No
+    bias (the pages write none).  Returns float64 q (T, Hq, d), k and v
+    (T, Hkv, d), unrotated.
+    """
+    x = decode_bf16(x)
+    T = x.shape[0]
+    q = (x @ decode_bf16(w_q)).reshape(T, n_q_heads, head_dim)
+    k = (x @ decode_bf16(w_k)).reshape(T, n_kv_heads, head_dim)
+    v = (x @ decode_bf16(w_v)).reshape(T, n_kv_heads, head_dim)
+    return q, k, v
+
+
+def frame_front_end(x, w_q, w_k, w_v, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                    positions, theta: float, scaling: float = 1.0):
+    """Projection then rotary embedding of q and k at the tokens' original
+    positions (paperlayer section 3.3: positions stay virtual; rainbus
+    prerequisites: one RoPE scaling for cache building and generation); v is
+    not rotated.  Returns float64 (q, k, v) before any rounding."""
+    q, k, v = project_frame(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    return (rope_at_positions(q, positions, theta, scaling),
+            rope_at_positions(k, positions, theta, scaling), v)
+
+
 def attention_mass_diagnostics(scores, n_history: int, budget: int, prev_kept=None):
     """The App. A measurements of one frame (paperlayer summary, App. A.1-A.3).
 

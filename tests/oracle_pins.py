@@ -383,6 +383,54 @@ def check_noncausal_closed_form() -> None:
                                           np.arange(min(B, (n + 1) * T)))
 
 
+def check_front_end() -> None:
+    """Q = X W_Q, K = X W_K, V = X W_V, then RoPE on q and k only.
+
+    Worked by hand: hidden = 2, one head of d = 2, x = [1, 2]; W_Q = I gives
+    q = [1, 2], W_K = [[0, 1], [1, 0]] gives k = [2, 1], W_V = [[1, 1],
+    [1, -1]] gives v = [3, -1]; at position 3 with d = 2 the only pair turns by
+    3 rad, so q becomes [cos 3 - 2 sin 3, sin 3 + 2 cos 3], k becomes
+    [2 cos 3 - sin 3, 2 sin 3 + cos 3] and v stays.  Brute force with scalar
+    loops on a random case; W_Q = I splits x into heads of d consecutive
+    features; at position 0 the front end equals the plain projection."""
+    x = np.array([[1.0, 2.0]])
+    wq = np.eye(2)
+    wk = np.array([[0.0, 1.0], [1.0, 0.0]])
+    wv = np.array([[1.0, 1.0], [1.0, -1.0]])
+    q, k, v = so.project_frame(x, wq, wk, wv, 1, 1, 2)
+    assert np.array_equal(q[0, 0], [1.0, 2.0]) and np.array_equal(k[0, 0], [2.0, 1.0])
+    assert np.array_equal(v[0, 0], [3.0, -1.0])
+    c3, s3 = math.cos(3.0), math.sin(3.0)
+    qr, kr, vr = so.frame_front_end(x, wq, wk, wv, 1, 1, 2, np.array([3]), 100.0)
+    assert np.allclose(qr[0, 0], [c3 - 2 * s3, s3 + 2 * c3], rtol=0, atol=1e-15), qr
+    assert np.allclose(kr[0, 0], [2 * c3 - s3, 2 * s3 + c3], rtol=0, atol=1e-15), kr
+    assert np.array_equal(vr[0, 0], [3.0, -1.0])
+    rng = np.random.default_rng(17)
+    T, Hq, Hkv, d = 3, 2, 1, 4
+    hidden = Hq * d
+    x = rng.standard_normal((T, hidden))
+    wq = rng.standard_normal((hidden, Hq * d))
+    wk = rng.standard_normal((hidden, Hkv * d))
+    wv = rng.standard_normal((hidden, Hkv * d))
+    q, k, v = so.project_frame(x, wq, wk, wv, Hq, Hkv, d)
+    for t in range(T):
+        for g in range(Hq):
+            for e in range(d):
+                ref = sum(x[t, i] * wq[i, g * d + e] for i in range(hidden))
+                assert abs(q[t, g, e] - ref) <= 1e-12, (t, g, e)
+        for h in range(Hkv):
+            for e in range(d):
+                assert abs(k[t, h, e] - sum(x[t, i] * wk[i, h * d + e] for i in range(hidden))) <= 1e-12
+                assert abs(v[t, h, e] - sum(x[t, i] * wv[i, h * d + e] for i in range(hidden))) <= 1e-12
+    qi, _, _ = so.project_frame(x, np.eye(hidden), wk, wv, Hq, Hkv, d)
+    for g in range(Hq):
+        assert np.array_equal(qi[:, g, :], x[:, g * d:(g + 1) * d])
+    q0, k0, v0 = so.frame_front_end(x, wq, wk, wv, Hq, Hkv, d, np.zeros(T), 1e6)
+    assert np.allclose(q0, q, rtol=0, atol=1e-15) and np.allclose(k0, k, rtol=0, atol=1e-15)
+    _, _, v9 = so.frame_front_end(x, wq, wk, wv, Hq, Hkv, d, np.arange(T) + 9, 1e4)
+    assert np.array_equal(v9, v)
+
+
 ALL_CHECKS = [
     check_hand_example,
     check_single_token_frame,
@@ -397,4 +445,5 @@ ALL_CHECKS = [
     check_attention_mass,
     check_shared_layer_ranking,
     check_noncausal_closed_form,
+    check_front_end,
 ]

@@ -289,3 +289,53 @@ def test_attention_mass_pin_catches_mutant(monkeypatch, mutant):
     monkeypatch.setattr(so, "attention_mass_diagnostics", mutant)
     with pytest.raises(AssertionError):
         oracle_pins.check_attention_mass()
+
+
+_orig_project = so.project_frame
+_orig_front = so.frame_front_end
+
+
+def project_k_v_swapped(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim):
+    q, k, v = _orig_project(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    return q, v, k
+
+
+def project_weights_transposed(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim):
+    x = so.decode_bf16(x)
+    T = x.shape[0]
+    q = (x @ so.decode_bf16(w_q).T).reshape(T, n_q_heads, head_dim)
+    _, k, v = _orig_project(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    return q, k, v
+
+
+def project_heads_interleaved(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim):
+    q, k, v = _orig_project(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    T = q.shape[0]
+    q = q.reshape(T, head_dim, n_q_heads).transpose(0, 2, 1)
+    return q, k, v
+
+
+def front_end_rotates_v(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim, positions, theta,
+                        scaling=1.0):
+    q, k, v = _orig_front(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim, positions, theta,
+                          scaling)
+    return q, k, so.rope_at_positions(v, positions, theta, scaling)
+
+
+def front_end_keys_unrotated(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim, positions, theta,
+                             scaling=1.0):
+    q, _, v = _orig_front(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim, positions, theta,
+                          scaling)
+    _, k, _ = _orig_project(x, w_q, w_k, w_v, n_q_heads, n_kv_heads, head_dim)
+    return q, k, v
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("project_frame", project_k_v_swapped), ("project_frame", project_weights_transposed),
+    ("project_frame", project_heads_interleaved), ("frame_front_end", front_end_rotates_v),
+    ("frame_front_end", front_end_keys_unrotated)],
+    ids=lambda v: v if isinstance(v, str) else v.__name__)
+def test_front_end_pin_catches_mutant(monkeypatch, name, mutant):
+    monkeypatch.setattr(so, name, mutant)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_front_end()
