@@ -35,6 +35,8 @@ Other measurements (not the headline line):
     --mode mass        App. A diagnostics (top-b historical mass, recency
                        mass, candidate-pool recall) of a layer that keeps
                        every token, averaged over --mass-frames frames
+    --mode frontend    the frame front end (q/k/v projection + RoPE) at the
+                       workload's shape, weights read from HBM
 """
 
 from __future__ import annotations
@@ -571,6 +573,59 @@ def run_mass(args):
 
 
 # ----------------------------------------------------------------------------
+# the frame front end: q, k, v = rope(X W_Q), rope(X W_K), X W_V
+# ----------------------------------------------------------------------------
+
+def run_frontend(args):
+    """Time statekv_qkv_rope at the workload's shape (hidden = Hq * d).  The
+    calls cycle through --frontend-layers distinct weight copies (together
+    larger than the 256 MB last-level cache), as the layers of a model would,
+    so that every call reads its weights from HBM."""
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload(args.workload)
+    T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+    hid = framegen.hidden_width(spec)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    w0 = up(framegen.projection_weights(spec))
+    ws = [w0] + [w0.clone() for _ in range(args.frontend_layers - 1)]
+    xs = [up(framegen.hidden_states(spec, n)) for n in range(8)]
+    outs = (torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev),
+            torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev),
+            torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev))
+    L = len(ws)
+    for i in range(args.warmup + L):
+        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    rows = (Hq + 2 * Hkv) * d
+    nbytes = rows * hid * 2 + T * hid * 2 + T * rows * 2
+    flops = 2.0 * T * hid * rows
+    print(json.dumps({
+        "mode": "frontend", "workload": args.workload, "tokens": T, "hidden": hid,
+        "out_features": rows, "weight_copies": L, "calls": args.steps,
+        "us_per_call": us, "algorithmic_bytes": nbytes,
+        "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+        "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "gflop": flops / 1e9, "tflops": flops / (us * 1e-6) / 1e12,
+        "frac_of_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS,
+        "timing": "HIP events around the calls on the launch stream",
+    }), flush=True)
+
+
+# ----------------------------------------------------------------------------
 # 28 layers of the 2B shape, layer-major per frame
 # ----------------------------------------------------------------------------
 
@@ -618,7 +673,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=0,
                     help="untimed frames after the state-fill frames (ceil(B/T), never timed)")
     ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode", "mass"],
+    ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode", "mass",
+                                       "frontend"],
                     default="headline")
     ap.add_argument("--decode-queries", type=int, nargs="+", default=[1, 4],
                     help="text tokens per decoding call (decode mode)")
@@ -642,6 +698,8 @@ def main(argv=None):
                          "D (positions), updated in place (inplace), or both")
     ap.add_argument("--mass-frames", type=int, default=64,
                     help="frames of the App. A diagnostics run (--mode mass)")
+    ap.add_argument("--frontend-layers", type=int, default=12,
+                    help="distinct weight copies the front-end timing cycles through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args(argv)
@@ -650,7 +708,7 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28,
-     "decode": run_decode, "mass": run_mass}[args.mode](args)
+     "decode": run_decode, "mass": run_mass, "frontend": run_frontend}[args.mode](args)
 
 
 if __name__ == "__main__":

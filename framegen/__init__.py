@@ -14,8 +14,12 @@ from .generator import (  # noqa: F401
     f64_to_bf16_bits,
     frame,
     frames,
+    hidden_states,
+    hidden_width,
+    projection_weights,
     rope_rotate,
     sink_plan,
+    split_projection_weights,
     stacked_frames,
     text_queries,
     workload,

@@ -229,6 +229,39 @@ def text_queries(spec: FrameSpec, n_tokens: int, index: int = 0) -> np.ndarray:
     return f64_to_bf16_bits(q)
 
 
+def hidden_width(spec: FrameSpec) -> int:
+    """Width of the visual-token hidden states entering the projection: the
+    pages give no model widths, so it is taken as Hq * d (which is the width
+    of the InternVL3-class backbones' language models)."""
+    return spec.n_q_heads * spec.head_dim
+
+
+def hidden_states(spec: FrameSpec, n: int) -> np.ndarray:
+    """Hidden states X_n of frame n's T visual tokens, (T, hidden) bf16 bits:
+    N(0, 1) draws from ``default_rng([seed, 2^31 - 2, n])``."""
+    rng = np.random.default_rng([spec.seed, 2**31 - 2, n])
+    return f64_to_bf16_bits(rng.standard_normal((spec.frame_tokens, hidden_width(spec))))
+
+
+def projection_weights(spec: FrameSpec) -> np.ndarray:
+    """The layer's projection weights packed output-major, bf16 bits of shape
+    ((Hq + 2 Hkv) d, hidden): row r holds the weights of output feature r,
+    rows ordered Q heads, K heads, V heads (d rows per head), so W_Q is the
+    transpose of rows [0, Hq d).  N(0, 1/hidden) draws (unit-variance
+    outputs for unit-variance inputs) from ``default_rng([seed, 2^31 - 3])``."""
+    hid = hidden_width(spec)
+    rows = (spec.n_q_heads + 2 * spec.n_kv_heads) * spec.head_dim
+    rng = np.random.default_rng([spec.seed, 2**31 - 3])
+    return f64_to_bf16_bits(rng.standard_normal((rows, hid)) / np.sqrt(hid))
+
+
+def split_projection_weights(spec: FrameSpec, w: np.ndarray):
+    """(W_Q, W_K, W_V) in the (hidden, out) orientation of Q = X W_Q, from
+    the packed output-major rows of projection_weights."""
+    qd, kd = spec.n_q_heads * spec.head_dim, spec.n_kv_heads * spec.head_dim
+    return w[:qd].T, w[qd:qd + kd].T, w[qd + kd:].T
+
+
 def frames(spec: FrameSpec, start: int = 0, stop: Optional[int] = None
            ) -> Iterator[Tuple[np.ndarray, np.ndarray, np.ndarray]]:
     """Frames start..stop-1 (default: all) as bfloat16 bit patterns."""

@@ -232,6 +232,35 @@ int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_quer
 int statekv_rope(statekv_layer* layer, void* x, int32_t n_tokens, int32_t n_heads,
                  int64_t first_position, void* stream);
 
+/* The frame front end: the frame's queries, keys and values from the hidden
+ * states of its visual tokens, Q_n = X_n W_Q, K_n = X_n W_K, V_n = X_n W_V
+ * (rainbus method steps; no bias), with q and k rotated at the tokens'
+ * original positions by the one RoPE configuration that cache building and
+ * generation share (paperlayer section 3.3; rainbus prerequisites, RoPE
+ * scaling).  Needs no layer; its outputs feed statekv_prefill_frame of a
+ * layer made with rope_theta = 0, with first_position = position_offset +
+ * n*T for frame n.
+ *   x: device, [n_tokens][hidden] bf16;
+ *   w: device, [(Hq + 2 Hkv) d][hidden] bf16, output-major: row r holds the
+ *      weights of output feature r; rows [0, Hq d) are W_Q transposed (query
+ *      head g = rows g d .. g d + d - 1), then W_K, then W_V, likewise;
+ *   q: device, [n_tokens][Hq][d] bf16, k and v: [n_tokens][Hkv][d] bf16,
+ *      written (must not overlap x or w);
+ *   token t sits at position first_position + t; rope_theta > 0 rotates q and
+ *   k (pairs (x_i, x_{i+d/2}), angle (p / rope_scaling) * rope_theta^(-2i/d),
+ *   rope_scaling <= 0 means 1); rope_theta = 0 leaves them unrotated.
+ * Arithmetic: fp32 accumulation of the bf16 products, the rotation in double
+ * from the fp32 sums, one rounding to bf16 (nearest, ties to even).
+ * Errors (host checks, nothing enqueued): STATEKV_ERR_INVALID_ARGUMENT for a
+ * null or misaligned pointer, a non-positive size, Hq not a multiple of Hkv,
+ * a negative first_position, rope_theta < 0, = 1 or not finite;
+ * STATEKV_ERR_UNSUPPORTED for d other than 64/128, hidden not a multiple of
+ * 64, or sizes beyond 2^20 tokens or features.  Asynchronous on stream. */
+int statekv_qkv_rope(const void* x, const void* w, int32_t n_tokens, int32_t hidden,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int64_t first_position, double rope_theta, double rope_scaling,
+                     void* q, void* k, void* v, void* stream);
+
 /* Views (host only; they enqueue nothing and never fail on a valid layer;
  * STATEKV_ERR_INVALID_ARGUMENT for a null argument).
  * statekv_state: the compressed state C_n, the fixed-capacity, importance-

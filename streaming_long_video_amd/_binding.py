@@ -113,6 +113,9 @@ def load_library() -> ctypes.CDLL:
         "statekv_full_attention_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int32, P, P]),
         "statekv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]),
+        "statekv_qkv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            ctypes.c_double, ctypes.c_double, P, P, P, P]),
         "statekv_state": (ctypes.c_int, [P, ctypes.POINTER(statekv_state_view)]),
         "statekv_detailed_cache": (ctypes.c_int, [P, ctypes.POINTER(statekv_cache_view)]),
         "statekv_reset_layer": (ctypes.c_int, [P]),
@@ -191,6 +194,14 @@ def statekv_rope(layer: int, x: int, n_tokens: int, n_heads: int, first_position
                  stream: int = 0) -> None:
     _check(load_library().statekv_rope(layer, x, n_tokens, n_heads, first_position,
                                        stream or None), "statekv_rope")
+
+
+def statekv_qkv_rope(x: int, w: int, n_tokens: int, hidden: int, n_q_heads: int,
+                     n_kv_heads: int, head_dim: int, first_position: int, rope_theta: float,
+                     rope_scaling: float, q: int, k: int, v: int, stream: int = 0) -> None:
+    _check(load_library().statekv_qkv_rope(x, w, n_tokens, hidden, n_q_heads, n_kv_heads,
+                                           head_dim, first_position, rope_theta, rope_scaling,
+                                           q, k, v, stream or None), "statekv_qkv_rope")
 
 
 def statekv_state(layer: int) -> statekv_state_view:

@@ -27,12 +27,14 @@ LIB = os.path.join(PKG, "libstatekv.so")
 SOURCES = [
     os.path.join(CSRC, "plan.cpp"),
     os.path.join(CSRC, "statekv_api.hip"),
+    os.path.join(CSRC, "frontend_api.hip"),
     os.path.join(CSRC, "kernels", "attention.hip"),
     os.path.join(CSRC, "kernels", "select.hip"),
     os.path.join(CSRC, "kernels", "gather.hip"),
     os.path.join(CSRC, "kernels", "decode.hip"),
     os.path.join(CSRC, "kernels", "rope.hip"),
     os.path.join(CSRC, "kernels", "diagnostics.hip"),
+    os.path.join(CSRC, "kernels", "frontend.hip"),
 ]
 
 ARCH = "gfx950"

@@ -17,24 +17,11 @@
 // One thread owns one (token, pair) and rotates it in every head, so the
 // trigonometry is done once per (token, pair).
 #include "../skv_internal.h"
+#include "bf16_device.h"
 
 namespace skv {
 
 namespace {
-
-__device__ inline float bf16_to_f32(uint16_t b) {
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
-// Nearest bf16 (8 significant bits, ties to even) of a finite double in the
-// float normal range (or zero): round the 52-bit fraction to 7 bits as an
-// integer, then the value converts to float exactly.
-__device__ inline uint16_t f64_to_bf16_rne(double y) {
-  uint64_t u = __builtin_bit_cast(uint64_t, y);
-  u += 0xFFFFFFFFFFFull + ((u >> 45) & 1u);
-  u &= ~((1ull << 45) - 1);
-  const float f = (float)__builtin_bit_cast(double, u);
-  return (uint16_t)(__builtin_bit_cast(uint32_t, f) >> 16);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs r) {
@@ -54,8 +41,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs r) {
     const uint16_t* x = first ? r.x : r.x2;
     uint16_t* y = first ? r.y : r.y2;
     const int64_t base = ((int64_t)t * nr + row) * D;
-    const double x0 = bf16_to_f32(x[base + i]);
-    const double x1 = bf16_to_f32(x[base + i + HALF]);
+    const double x0 = bf16_bits_to_f32(x[base + i]);
+    const double x1 = bf16_bits_to_f32(x[base + i + HALF]);
     y[base + i] = f64_to_bf16_rne(fma(x0, c, -(x1 * s)));
     y[base + i + HALF] = f64_to_bf16_rne(fma(x0, s, x1 * c));
   }

@@ -173,6 +173,20 @@ hipError_t launch_rope(const RopeArgs& r, int D, const Stream& st);
 
 hipError_t launch_full_combine(const AttnArgs& a, float* o, int D, const Stream& st);
 
+// The frame's q/k/v projection with RoPE (front end): q = rope(X W_Q),
+// k = rope(X W_K), v = X W_V.
+struct FrontArgs {
+  const uint16_t* x;  // [T][hidden] bf16 hidden states
+  const uint16_t* w;  // [(Hq + 2 Hkv) D][hidden] bf16, rows: Q heads, K heads, V heads
+  uint16_t* q;        // [T][Hq][D] bf16
+  uint16_t* k;        // [T][Hkv][D] bf16
+  uint16_t* v;        // [T][Hkv][D] bf16
+  int T, hidden, Hq, Hkv;
+  int64_t first_position;  // position of token 0
+  double theta, scaling;   // theta <= 0: no rotation
+};
+hipError_t launch_qkv_rope(const FrontArgs& a, int D, const Stream& st);
+
 // App. A diagnostics of the last frame (one workgroup per budget).
 constexpr int kMaxMassBudgets = 64;
 struct MassArgs {

@@ -210,6 +210,30 @@ class Layer:
             pass
 
 
+def qkv_rope(x: torch.Tensor, w: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim: int,
+             first_position: int, rope_theta: float, rope_scaling: float = 0.0,
+             out=None, stream=None):
+    """The library's frame front end: q, k, v = rope(X W_Q), rope(X W_K), X W_V.
+    x: [T][hidden] bf16; w: [(Hq + 2 Hkv) d][hidden] bf16 (output-major, rows
+    Q heads, K heads, V heads).  Returns (q, k, v) bf16 [T][H][d] tensors."""
+    T, hidden = x.shape
+    rows = (n_q_heads + 2 * n_kv_heads) * head_dim
+    for name, t, shape in (("x", x, (T, hidden)), ("w", w, (rows, hidden))):
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 tensor of shape {shape}")
+    if w.device != x.device:
+        raise ValueError("x and w must be on one device")
+    if out is None:
+        out = (torch.empty((T, n_q_heads, head_dim), dtype=torch.bfloat16, device=x.device),
+               torch.empty((T, n_kv_heads, head_dim), dtype=torch.bfloat16, device=x.device),
+               torch.empty((T, n_kv_heads, head_dim), dtype=torch.bfloat16, device=x.device))
+    q, k, v = out
+    B.statekv_qkv_rope(x.data_ptr(), w.data_ptr(), T, hidden, n_q_heads, n_kv_heads, head_dim,
+                       int(first_position), float(rope_theta), float(rope_scaling),
+                       q.data_ptr(), k.data_ptr(), v.data_ptr(), _stream_ptr(stream))
+    return q, k, v
+
+
 def select_topb(scores: torch.Tensor, budget: int, stream=None) -> torch.Tensor:
     """The library's top-B select on a float32 device vector (ascending indices)."""
     if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():

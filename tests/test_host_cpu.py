@@ -234,6 +234,24 @@ def test_select_argument_errors():
         B.statekv_select_topb(1 << 40, 0, 5, 1 << 40)
 
 
+def test_front_end_argument_errors_are_host_side():
+    """statekv_qkv_rope rejects bad arguments before any launch (fake,
+    16-byte aligned device addresses: nothing is dereferenced)."""
+    a = 1 << 40
+    good = dict(x=a, w=a, n_tokens=256, hidden=3584, n_q_heads=28, n_kv_heads=4, head_dim=128,
+                first_position=0, rope_theta=1e6, rope_scaling=1.0, q=a, k=a, v=a)
+    bad = [(dict(x=0), -1), (dict(q=a + 2), -1), (dict(n_tokens=0), -1), (dict(hidden=-64), -1),
+           (dict(n_q_heads=27), -1), (dict(first_position=-1), -1), (dict(rope_theta=-1.0), -1),
+           (dict(rope_theta=1.0), -1), (dict(rope_theta=float("inf")), -1),
+           (dict(rope_scaling=float("nan")), -1), (dict(head_dim=96), -2),
+           (dict(hidden=3584 + 32), -2), (dict(n_tokens=(1 << 20) + 1), -2)]
+    for change, status in bad:
+        args = dict(good, **change)
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_qkv_rope(**args)
+        assert e.value.status == status, change
+
+
 def test_status_strings():
     assert B.statekv_status_string(0) == "ok"
     assert "capacity" in B.statekv_status_string(-4)
