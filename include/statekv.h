@@ -223,6 +223,22 @@ int statekv_full_attention_frame(statekv_layer* layer, const void* q, const void
 int statekv_decode_attention(statekv_layer* layer, const void* q, int32_t n_queries, float* o,
                              void* stream);
 
+/* statekv_decode_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split partials in a
+ * fixed 8 MiB device array of the library (one per GPU, kept until the
+ * process ends) instead of the layer's workspace; it calls no allocator.
+ * Results are bit-identical to statekv_decode_attention whenever the split
+ * count that one chooses fits the array (every G * n_queries <= 32 case of
+ * up to 64 query heads of d <= 128); otherwise fewer splits are used.  All
+ * calls on one GPU share the array: calls that overlap on one GPU (on
+ * different streams, or from several host threads) race and must be
+ * serialised by the caller.  Same arguments, preconditions and errors as
+ * statekv_decode_attention, plus STATEKV_ERR_HIP if the array's device
+ * address cannot be resolved. */
+int statekv_decode_attention_noalloc(statekv_layer* layer, const void* q, int32_t n_queries,
+                                     float* o, void* stream);
+
 /* Rotate n_tokens x n_heads rows of d bf16 values in place (device,
  * [n_tokens][n_heads][d], 16-byte aligned) at positions first_position + i,
  * with the layer's rope_theta and rope_scaling (text queries before

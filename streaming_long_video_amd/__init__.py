@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     make_config,
     statekv_attention_mass,
     statekv_decode_attention,
+    statekv_decode_attention_noalloc,
     statekv_detailed_cache,
     statekv_free_layer,
     statekv_full_attention_frame,

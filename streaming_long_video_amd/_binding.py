@@ -112,6 +112,7 @@ def load_library() -> ctypes.CDLL:
         "statekv_prefill_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_full_attention_frame": (ctypes.c_int, [P, P, P, P, P, P]),
         "statekv_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int32, P, P]),
+        "statekv_decode_attention_noalloc": (ctypes.c_int, [P, P, ctypes.c_int32, P, P]),
         "statekv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]),
         "statekv_qkv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -188,6 +189,13 @@ def statekv_full_attention_frame(layer: int, q: int, k: int, v: int, o: int,
 def statekv_decode_attention(layer: int, q: int, n_queries: int, o: int, stream: int = 0) -> None:
     _check(load_library().statekv_decode_attention(layer, q, n_queries, o, stream or None),
            "statekv_decode_attention")
+
+
+def statekv_decode_attention_noalloc(layer: int, q: int, n_queries: int, o: int,
+                                     stream: int = 0) -> None:
+    _check(load_library().statekv_decode_attention_noalloc(layer, q, n_queries, o,
+                                                           stream or None),
+           "statekv_decode_attention_noalloc")
 
 
 def statekv_rope(layer: int, x: int, n_tokens: int, n_heads: int, first_position: int,

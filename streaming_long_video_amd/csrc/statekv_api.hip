@@ -8,6 +8,7 @@
 // from the device.
 #include <math.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -23,6 +24,7 @@ struct ProfRecord {
 struct statekv_layer {
   skv::Plan plan;
   char* ws;          // device workspace base
+  int device;        // device current at init (the workspace's)
   int64_t n;         // frames seen
   int32_t c;         // live compressed-state rows
   int32_t cur;       // index (0/1) of the buffer holding C_n
@@ -37,6 +39,34 @@ struct statekv_layer {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Device scratch of statekv_decode_attention_noalloc: the decoding kernels'
+// split partials (row max, row sum, O) for callers that cannot allocate.
+// Every GPU holds its own copy for the life of the process; host code never
+// passes the array's name to a kernel (on the host it only names the
+// symbol), only the per-device address resolved below.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+bool scratch_done[kMaxDevices];
+hipError_t scratch_status[kMaxDevices];
+void* scratch_ptr[kMaxDevices];
+
+// Resolves the device address of `scratch` once per device, with that device
+// current (the caller's).  Returns the cached status of that one call.
+hipError_t resolve_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_done[dev]) {
+    void* ptr = nullptr;
+    scratch_status[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_status[dev] == hipSuccess ? ptr : nullptr;
+    scratch_done[dev] = true;
+  }
+  return scratch_status[dev];
+}
 
 template <class T>
 T* at(const statekv_layer* L, size_t off) {
@@ -125,10 +155,17 @@ int statekv_init_layer(const statekv_layer_config* cfg, void* d_workspace, size_
   if (st != STATEKV_OK) return st;
   if (workspace_bytes < p.total) return STATEKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(d_workspace) & 255u) return STATEKV_ERR_WORKSPACE;
+  // the no-allocation decoding entry point's scratch on the current device
+  // (the workspace's); a failure here only affects that entry point, which
+  // reports it, and without a device the address is resolved on its first call
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess) (void)resolve_scratch(dev);
+  else dev = -1;
   statekv_layer* L = new (std::nothrow) statekv_layer();
   if (!L) return STATEKV_ERR_INVALID_ARGUMENT;
   L->plan = p;
   L->ws = static_cast<char*>(d_workspace);
+  L->device = dev;
   L->n = 0;
   L->c = 0;
   L->cur = 0;
@@ -311,26 +348,24 @@ int statekv_full_attention_frame(statekv_layer* L, const void* q, const void* k,
   return STATEKV_OK;
 }
 
-int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries, float* o,
-                             void* stream) {
-  if (!L || !q || !o || n_queries < 1) return STATEKV_ERR_INVALID_ARGUMENT;
-  if (!aligned16(q) || !aligned16(o)) return STATEKV_ERR_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+// Decoding over D with the split partials at m_part / l_part ([parts][Hq][M]
+// floats each) and o_part ([parts][M][Hq][D] floats), room for max_parts
+// workgroup partials.
+int decode_into(statekv_layer* L, const void* q, int32_t n_queries, float* o, void* stream,
+                float* m_part, float* l_part, float* o_part, int64_t max_parts) {
   const skv::Plan& p = L->plan;
-  if (p.G * (int64_t)n_queries > 32) return STATEKV_ERR_UNSUPPORTED;
   const int64_t hist = L->n * (int64_t)p.T;
   const int64_t len = hist < p.cap ? hist : p.cap;
   if (len <= 0) return STATEKV_ERR_INVALID_ARGUMENT;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   // splits (one wave each): about two waves per SIMD over all KV heads, at
-  // least 32 keys per wave; the workgroup partials (four splits each) must fit
-  // the split-partial regions of the workspace
+  // least 32 keys per wave, at most four per workgroup partial
   const int64_t want = (2048 + p.Hkv - 1) / p.Hkv;
   const int64_t by_len = (len + 31) / 32;
-  const int64_t opart = p.splits > p.full_splits ? p.splits : p.full_splits;
-  const int64_t parts_o = opart * p.T / n_queries;
-  const int64_t parts_ml = (int64_t)p.part_splits * p.tpad / n_queries;
-  int64_t max_parts = parts_o < parts_ml ? parts_o : parts_ml;
   if (max_parts > skv::kMaxDecodeParts) max_parts = skv::kMaxDecodeParts;
   int64_t ns = want < by_len ? want : by_len;
   if (ns > 4 * max_parts) ns = 4 * max_parts;
@@ -339,9 +374,9 @@ int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries,
   d.q = static_cast<const uint16_t*>(q);
   d.kd = at<uint16_t>(L, p.off_dk);
   d.vd = at<uint16_t>(L, p.off_dv);
-  d.m_part = at<float>(L, p.off_m);
-  d.l_part = at<float>(L, p.off_l);
-  d.o_part = at<float>(L, p.off_o);
+  d.m_part = m_part;
+  d.l_part = l_part;
+  d.o_part = o_part;
   d.cap = p.cap;
   d.len = len;
   d.M = n_queries;
@@ -356,6 +391,60 @@ int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries,
     e = timed(L, STATEKV_KERNEL_SPLIT_SUM, st,
               [&](const skv::Stream& ks) { return skv::launch_decode_merge(d, o, p.D, ks); });
   return hip_status(e);
+}
+
+int check_decode_args(const statekv_layer* L, const void* q, int32_t n_queries, const float* o) {
+  if (!L || !q || !o || n_queries < 1) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(o)) return STATEKV_ERR_INVALID_ARGUMENT;
+  if (L->plan.G * (int64_t)n_queries > 32) return STATEKV_ERR_UNSUPPORTED;
+  if (L->n < 1) return STATEKV_ERR_INVALID_ARGUMENT;
+  return STATEKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int statekv_decode_attention(statekv_layer* L, const void* q, int32_t n_queries, float* o,
+                             void* stream) {
+  const int chk = check_decode_args(L, q, n_queries, o);
+  if (chk != STATEKV_OK) return chk;
+  const skv::Plan& p = L->plan;
+  // the workgroup partials live in the workspace's split-partial regions
+  const int64_t opart = p.splits > p.full_splits ? p.splits : p.full_splits;
+  const int64_t parts_o = opart * p.T / n_queries;
+  const int64_t parts_ml = (int64_t)p.part_splits * p.tpad / n_queries;
+  const int64_t max_parts = parts_o < parts_ml ? parts_o : parts_ml;
+  return decode_into(L, q, n_queries, o, stream, at<float>(L, p.off_m), at<float>(L, p.off_l),
+                     at<float>(L, p.off_o), max_parts);
+}
+
+int statekv_decode_attention_noalloc(statekv_layer* L, const void* q, int32_t n_queries,
+                                     float* o, void* stream) {
+  const int chk = check_decode_args(L, q, n_queries, o);
+  if (chk != STATEKV_OK) return chk;
+  const skv::Plan& p = L->plan;
+  if (L->device < 0) {  // no device was current at init: take the current one now
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return STATEKV_ERR_HIP;
+    L->device = dev;
+  }
+  if (resolve_scratch(L->device) != hipSuccess) return STATEKV_ERR_HIP;
+  char* base = static_cast<char*>(scratch_ptr[L->device]);
+  // carve [parts][Hq][M] row maxima, the same for row sums, then
+  // [parts][M][Hq][D] O partials out of the fixed scratch
+  const size_t rows = (size_t)p.Hq * (size_t)n_queries;
+  const size_t per_part = rows * (2 + (size_t)p.D) * sizeof(float);
+  const size_t room = kNoAllocScratchBytes - 2 * 256;
+  const int64_t max_parts = (int64_t)(room / per_part);
+  if (max_parts < 1) return STATEKV_ERR_UNSUPPORTED;  // cannot happen for G*M <= 32, Hkv < 500
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t ml_bytes = up((size_t)max_parts * rows * sizeof(float));
+  float* m_part = reinterpret_cast<float*>(base);
+  float* l_part = reinterpret_cast<float*>(base + ml_bytes);
+  float* o_part = reinterpret_cast<float*>(base + 2 * ml_bytes);
+  if (2 * ml_bytes + (size_t)max_parts * rows * p.D * sizeof(float) > kNoAllocScratchBytes)
+    return STATEKV_ERR_UNSUPPORTED;
+  return decode_into(L, q, n_queries, o, stream, m_part, l_part, o_part, max_parts);
 }
 
 int statekv_rope(statekv_layer* L, void* x, int32_t n_tokens, int32_t n_heads,
