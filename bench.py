@@ -26,7 +26,8 @@ CPU oracle timed on a bounded sample of the same stream.
 
 Other measurements (not the headline line):
     --mode crossover   StateKV vs quadratic full attention, 1B shape,
-                       B in {1024, 2048, 4096}, N in {32, ..., 512}
+                       B in {1024, 2048, 4096}, N in {2, 4, ..., 512}, and
+                       the frames where time and FLOPs cross over
     --mode depth28     28 independent 2B-shaped layers, layer-major per
                        frame, per-frame latency at frames 1, 9, 65, 256
     --mode decode      decoding attention over the detailed state after the
@@ -411,6 +412,11 @@ def run_headline(args):
 # ----------------------------------------------------------------------------
 
 def run_crossover(args):
+    """StateKV against quadratic full attention at the 1B shape: per-frame time
+    of every frame n < 512 for each budget (HIP events between frames), the
+    marginal and cumulative time at N in {2, 4, ..., 512}, and the first frame
+    from which full attention's per-frame time stays above StateKV's (the time
+    crossover) beside the FLOP crossover."""
     import torch
 
     import framegen
@@ -418,7 +424,7 @@ def run_crossover(args):
 
     spec = framegen.workload("crossover_1b")
     T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
-    Ns = [32, 64, 128, 256, 512]
+    Ns = [2, 4, 8, 16, 32, 64, 128, 256, 512]
     Nmax = max(Ns)
     qs, ks, vs = framegen.stacked_frames(spec, 0, Nmax, workers=gen_workers(args))
     dev = torch.device("cuda", 0)
@@ -428,45 +434,57 @@ def run_crossover(args):
 
     q_all, k_all, v_all = up(qs), up(ks), up(vs)
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
-    rows = []
-    # StateKV: per-frame time of every frame (events around each call)
-    for B in (1024, 2048, 4096):
-        layer = skv.Layer(Hq, Hkv, d, T, B, detailed_capacity=Nmax * T)
+
+    def per_frame(call):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(Nmax + 1)]
         ev[0].record()
         for n in range(Nmax):
-            layer.prefill(q_all[n], k_all[n], v_all[n], out=out)
+            call(n)
             ev[n + 1].record()
         torch.cuda.synchronize()
-        per = np.array([ev[n].elapsed_time(ev[n + 1]) for n in range(Nmax)])
+        return np.array([ev[n].elapsed_time(ev[n + 1]) for n in range(Nmax)])
+
+    def first_stays_above(a, b):
+        """first n from which a[m] > b[m] for every m >= n (None if never)"""
+        above = a > b
+        for n in range(len(a)):
+            if above[n:].all():
+                return n
+        return None
+
+    # quadratic full attention: frame n attends over all n*T earlier tokens
+    layer = skv.Layer(Hq, Hkv, d, T, 1024, detailed_capacity=Nmax * T)
+    full = per_frame(lambda n: layer.full_attention(q_all[n], k_all[n], v_all[n], out=out))
+    layer.close()
+    full_flops = np.array([useful_attention_flops(Hq, d, T, n * T) for n in range(Nmax)])
+    rows, crossings = [], {}
+    for B in (1024, 2048, 4096):
+        layer = skv.Layer(Hq, Hkv, d, T, B, detailed_capacity=Nmax * T, num_splits=args.splits)
+        per = per_frame(lambda n: layer.prefill(q_all[n], k_all[n], v_all[n], out=out))
+        layer.close()
+        flops = np.array([useful_attention_flops(Hq, d, T, min(B, n * T)) for n in range(Nmax)])
+        crossings[str(B)] = {
+            "time_frame": first_stays_above(full, per),
+            "flop_frame": first_stays_above(full_flops, flops),
+        }
         for N in Ns:
             steady = per[min(B // T + 1, N - 1):N]
             rows.append({"method": "statekv", "B": B, "N": N,
                          "ms_per_frame_steady": float(np.mean(steady)),
                          "ms_last_frame": float(per[N - 1]),
                          "ms_cumulative": float(per[:N].sum()),
-                         "gflop_last_frame": useful_attention_flops(Hq, d, T, min(B, (N - 1) * T))
-                         / 1e9,
-                         "gflop_cumulative": sum(useful_attention_flops(Hq, d, T, min(B, n * T))
-                                                 for n in range(N)) / 1e9})
-        layer.close()
-    # quadratic full attention: frame n attends over all n*T earlier tokens
-    layer = skv.Layer(Hq, Hkv, d, T, 1024, detailed_capacity=Nmax * T)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(Nmax + 1)]
-    ev[0].record()
-    for n in range(Nmax):
-        layer.full_attention(q_all[n], k_all[n], v_all[n], out=out)
-        ev[n + 1].record()
-    torch.cuda.synchronize()
-    per = np.array([ev[n].elapsed_time(ev[n + 1]) for n in range(Nmax)])
+                         "gflop_last_frame": float(flops[N - 1]) / 1e9,
+                         "gflop_cumulative": float(flops[:N].sum()) / 1e9})
     for N in Ns:
         rows.append({"method": "full_attention", "N": N,
-                     "ms_last_frame": float(per[N - 1]),
-                     "ms_cumulative": float(per[:N].sum()),
-                     "gflop_last_frame": useful_attention_flops(Hq, d, T, (N - 1) * T) / 1e9,
-                     "gflop_cumulative": sum(useful_attention_flops(Hq, d, T, n * T)
-                                             for n in range(N)) / 1e9})
-    print(json.dumps({"mode": "crossover", "workload": "crossover_1b", "rows": rows}), flush=True)
+                     "ms_last_frame": float(full[N - 1]),
+                     "ms_cumulative": float(full[:N].sum()),
+                     "gflop_last_frame": float(full_flops[N - 1]) / 1e9,
+                     "gflop_cumulative": float(full_flops[:N].sum()) / 1e9})
+    print(json.dumps({"mode": "crossover", "workload": "crossover_1b",
+                      "splits": args.splits or "auto",
+                      "timing": "HIP events between consecutive frames on the launch stream",
+                      "crossover": crossings, "rows": rows}), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -646,7 +664,8 @@ def run_depth28(args):
         qs, ks, vs = framegen.stacked_frames(s, 0, N, workers=gen_workers(args))
         up = lambda x: torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         frames.append((up(qs), up(ks), up(vs)))
-        layers.append(skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T))
+        layers.append(skv.Layer(Hq, Hkv, d, T, Bs, detailed_capacity=N * T,
+                                num_splits=args.splits))
     out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(N + 1)]
     ev[0].record()
@@ -659,6 +678,7 @@ def run_depth28(args):
     per = [ev[n].elapsed_time(ev[n + 1]) for n in range(N)]
     pick = {f"frame_{n + 1}": per[n] for n in (0, 8, 64, N - 1)}
     print(json.dumps({"mode": "depth28", "workload": "internvl3_2b_28layers",
+                      "splits": args.splits or "auto",
                       "ms_per_frame_all_layers": pick,
                       "ms_mean_steady": float(np.mean(per[Bs // T + 1:])),
                       "ms_first_frame": per[0]}), flush=True)

@@ -500,7 +500,12 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
               oacc[i][mb], 0, 0, 0);
   };
 
-  // pass 1: online row max / sum of exp over this block
+  // pass 1: row sum of exp over this block relative to a reference maximum
+  // mrun.  The reference only moves when a block's sum shows it was exceeded
+  // by more than 2^32 (or before the row has seen a visible key): then the
+  // block's maximum is taken exactly and the running sum rescaled.  Logits
+  // below the reference only shrink their terms, so the (reference, sum)
+  // pair describes the same log-sum-exp as the exact running maximum would.
   auto stats_block = [&](const f32x16 (&sacc)[QB], int kbase, bool masked) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
@@ -508,23 +513,31 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         z[r] = (!masked || visible(kbase, i, r)) ? sacc[i][r] : -INFINITY;
-      float m8[8];
+      auto block_sum = [&](float ms) __attribute__((always_inline)) {
+        float e[16];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) m8[r] = fmaxf(z[2 * r], z[2 * r + 1]);
-      const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                             fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-      const float mnew = fmaxf(mrun[i], mx);
-      // nothing visible yet for this lane: every exp below is exp2(-inf) = 0
-      const float ms = (mnew == -INFINITY ? 0.f : mnew) * sl2;
-      float e[16];
+        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(z[r], sl2, -ms));
+        for (int st = 8; st >= 1; st >>= 1)
 #pragma unroll
-      for (int st = 8; st >= 1; st >>= 1)
+          for (int r = 0; r < st; ++r) e[r] += e[r + st];
+        return e[0];
+      };
+      const float sum = block_sum(mrun[i] == -INFINITY ? 0.f : mrun[i] * sl2);
+      if (mrun[i] == -INFINITY || !(sum <= 0x1p32f)) {
+        float m8[8];
 #pragma unroll
-        for (int r = 0; r < st; ++r) e[r] += e[r + st];
-      lrun[i] = lrun[i] * __builtin_amdgcn_exp2f(fmaf(mrun[i], sl2, -ms)) + e[0];
-      mrun[i] = mnew;
+        for (int r = 0; r < 8; ++r) m8[r] = fmaxf(z[2 * r], z[2 * r + 1]);
+        const float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                               fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        const float mnew = fmaxf(mrun[i], mx);
+        // nothing visible yet for this lane: every exp below is exp2(-inf) = 0
+        const float ms = (mnew == -INFINITY ? 0.f : mnew) * sl2;
+        lrun[i] = lrun[i] * __builtin_amdgcn_exp2f(fmaf(mrun[i], sl2, -ms)) + block_sum(ms);
+        mrun[i] = mnew;
+      } else {
+        lrun[i] += sum;
+      }
     }
   };
 
@@ -699,20 +712,69 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
     // key tiles of this split that no query of the row tile can see
     for (int j = tile_end * KT + tid; j < min(tile_hi * KT, pool); j += kThreads)
       a.sig_part[((int64_t)h * a.rt + rtile) * a.ldsig + j] = 0.f;
-    // O^T[d = 32mb + 8(r/4) + 4 half + r%4][query] -> O[t][g][d]; split
-    // partials keep P's 2^12 (the sum of the splits removes it), a single
-    // split is the output itself
-    const float oscale = a.S == 1 ? kPUnscale : 1.f;
+    // O^T[d = 32mb + 8(r/4) + 4 half + r%4][query] -> O[t][g][d], P's 2^12
+    // removed (exactly: a power of 2).  A single split is the output itself;
+    // several write fp32 partials [S][T][Hq][d] that the select launch sums
+    // in split order
 #pragma unroll
     for (int i = 0; i < QB; ++i) {
-      if (qtok[i] < 0) continue;
-      float* dst = a.o_out + ((int64_t)(a.S == 1 ? 0 : s) * a.T + qtok[i]) * a.Hq * D +
-                   (int64_t)qhead[i] * D;
-      if (a.S == 1) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= oscale;
+      for (int mb = 0; mb < NMB; ++mb) oacc[i][mb] *= kPUnscale;
+      if (a.S > 1) {
+        // this split's partial [S][T][Hq][d], stored row-major through a
+        // wave-private slice of the idle K (waves 0-3) or V^T (waves 4-7)
+        // tile buffers: a lane holds one query's d values column-wise, so
+        // direct stores would write 32-byte pieces of 32 rows each; via LDS
+        // every store instruction writes whole rows.  Non-temporal: the lines
+        // stream out instead of staying dirty in L2 until the kernel ends.
+        // kCR d values per round.
+        // Every lane of the wave takes part (a lane stores pieces of other
+        // lanes' rows); the block's validity is uniform over the wave.
+        constexpr int kCR = D == 128 ? 64 : 32;
+        constexpr int kOLd = kCR + 4;  // floats per staged row (16-byte aligned)
+        constexpr int kPerRow = kCR / 4;  // 16-byte pieces per row and round
+        static_assert(4 * 32 * kOLd * 4 <= (int)sizeof(Ks), "K tile buffers hold 4 slices");
+        static_assert(4 * 32 * kOLd * 4 <= (int)sizeof(Vt), "V tile buffers hold 4 slices");
+        static_assert(32 * kPerRow % 64 == 0, "whole store instructions per round");
+        const int b = b0 + w * QB + i;
+        if (b >= a.nqblk) continue;
+        const int tok0 = (b / a.G) * kTokBlk;  // the block's tokens: tok0 + lane row
+        const int qh = h * a.G + b % a.G;
+        float* ot = reinterpret_cast<float*>(w < 4 ? (void*)&Ks[0][0] : (void*)&Vt[0][0]) +
+                    (w & 3) * 32 * kOLd;
+        float* dst = a.o_out + ((int64_t)s * a.T * a.Hq + qh) * D;
+#pragma unroll
+        for (int h2 = 0; h2 < D / kCR; ++h2) {
+#pragma unroll
+          for (int m2 = 0; m2 < kCR / 32; ++m2) {
+            const int mb = (kCR / 32) * h2 + m2;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              f32x4 v = {oacc[i][mb][4 * q4], oacc[i][mb][4 * q4 + 1], oacc[i][mb][4 * q4 + 2],
+                         oacc[i][mb][4 * q4 + 3]};
+              *reinterpret_cast<f32x4*>(ot + l32 * kOLd + m2 * 32 + 8 * q4 + 4 * half) = v;
+            }
+          }
+          // LDS accesses of one wave complete in order; keep the compiler
+          // from moving the reads above the writes (or the next round's
+          // writes above these reads)
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int u = 0; u < 32 * kPerRow / 64; ++u) {
+            const int p = u * 64 + lane;
+            const int r = p / kPerRow, c4 = p % kPerRow;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ot + r * kOLd + c4 * 4);
+            if (tok0 + r < a.T)
+              __builtin_nontemporal_store(
+                  v, reinterpret_cast<f32x4*>(dst + (int64_t)(tok0 + r) * a.Hq * D + kCR * h2 + c4 * 4));
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+        continue;
       }
-      if (a.S == 1 && a.out_bf16) {  // the output itself, as bf16 (same element offsets)
+      if (qtok[i] < 0) continue;
+      float* dst = a.o_out + ((int64_t)qtok[i] * a.Hq + qhead[i]) * D;
+      if (a.out_bf16) {  // the output itself, as bf16 (same element offsets)
         __bf16* dst16 = reinterpret_cast<__bf16*>(a.o_out) + ((int64_t)qtok[i] * a.Hq + qhead[i]) * D;
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)

@@ -18,18 +18,17 @@
 // epilogue holds both members of every pair.  Wave (wm, wn) computes tokens
 // 32 wm.. x the pair's first (wn = 0) or second (wn = 1) members with
 // v_mfma_f32_32x32x16_bf16 (tokens on M, features on N, fp32 accumulation).
-// Hidden features are staged in 64-wide chunks through LDS, double-buffered
-// (next chunk's global loads in registers while the current one is
-// computed).  Workgroup ids are renumbered so the token tiles of one feature
+// Hidden features stream through LDS in 64-wide chunks (8 KB of X, 8 KB of
+// W) by direct global-to-LDS loads (global_load_lds_dwordx4, no registers),
+// in a ring of kFeStages stages: kFeStages - 1 chunks are in flight while one
+// is computed, with one barrier per chunk and waits counted per chunk (a
+// barrier without a fence, so the loads still in flight are not drained).
+// In LDS a staged row is 128 bytes with its 16-byte pieces XOR-swizzled by
+// (row / 2) mod 8 -- chosen on the global side, since a direct load writes
+// its 64 lanes' pieces contiguously -- so the operand reads are free of bank
+// conflicts.  Workgroup ids are renumbered so the token tiles of one feature
 // tile run on the same XCD and share its weight rows in that XCD's L2.
 //
-// Epilogue.  The accumulators go through LDS so that each thread holds one
-// pair index j for 8 consecutive tokens; cos/sin of the angle
-// (p / scaling) * theta^(-2i/d) are formed in double precision (p reaches
-// 1e5 and beyond: a float angle would be off by ~1e-2 rad) for the first
-// token and stepped by an exact-angle rotation for the next ones; the
-// rotation is done in double from the fp32 accumulators and rounded once to
-// bf16 (nearest, ties to even).  V heads are rounded without rotation.
 #include "../skv_internal.h"
 #include "bf16_device.h"
 
@@ -39,17 +38,26 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kFeM = 64;         // tokens per tile
-constexpr int kFeN = 64;         // output features per tile (32 rotation pairs)
-constexpr int kFeK = 64;         // hidden features per staged chunk
-constexpr int kFeThreads = 256;  // 4 waves
-constexpr int kFeLd = kFeK + 8;  // bf16 per staged row (conflict-free 16-byte reads)
-constexpr int kFeOld = kFeN + 1; // floats per row of the epilogue tile
-constexpr int kFePieces = kFeM * kFeK / 8 / kFeThreads;  // 16-byte pieces / thread / operand
-static_assert(kFePieces * kFeThreads * 8 == kFeM * kFeK, "X chunk splits evenly");
-static_assert(kFeN == kFeM, "one piece count serves both operands");
+constexpr int kFeM = 64;          // tokens per tile
+constexpr int kFeN = 64;          // output features per tile (32 rotation pairs)
+constexpr int kFeK = 64;          // hidden features per staged chunk (128-byte rows)
+constexpr int kFeThreads = 256;   // 4 waves
+constexpr int kFeStages = 4;      // LDS ring: chunks in flight + the one computed
+constexpr int kFeOld = kFeN + 1;  // floats per row of the epilogue tile
+constexpr int kFeRows = kFeM + kFeN;  // staged rows per chunk (X rows, then W rows)
+constexpr int kFeStage = kFeRows * kFeK;  // bf16 per stage (16 KB)
+// direct loads per wave per chunk: a load covers 8 rows (64 lanes x 16 B)
+constexpr int kFeLoads = kFeRows / 8 / (kFeThreads / 64);
+static_assert(kFeLoads * 8 * (kFeThreads / 64) == kFeRows, "rows split evenly over the waves");
+// s_waitcnt operand: vmcnt(n) with expcnt and lgkmcnt left alone
+constexpr int kWaitVm = 0x0F70;
+
+#define FE_GLOBAL(p) ((const void __attribute__((address_space(1)))*)(p))
+#define FE_LDS(p) ((void __attribute__((address_space(3)))*)(p))
+
+// 16-byte piece `c` of staged row `r` sits in slot c ^ ((r / 2) mod 8)
+__device__ inline int fe_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 // Workgroups are dealt to the 8 XCDs round-robin; renumber them so each XCD
 // gets a contiguous range of logical ids (the token tiles of a feature tile
@@ -60,15 +68,11 @@ __device__ inline int fe_logical_id(int b, int n) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kFeThreads) void qkv_rope_kernel(FrontArgs a) {
+__global__ __launch_bounds__(kFeThreads, 2) void qkv_rope_kernel(FrontArgs a) {
   constexpr int HALF = D / 2;
   constexpr int TPH = HALF / 32;  // feature tiles per head
-  constexpr int kStageBytes = 2 * 2 * kFeM * kFeLd * 2;
-  constexpr int kTileBytes = kFeM * kFeOld * 4;
-  static_assert(kTileBytes <= kStageBytes, "epilogue tile fits in the staging buffers");
-  __shared__ __attribute__((aligned(16))) char smem[kStageBytes];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);        // [2][kFeM][kFeLd]
-  uint16_t* ws = xs + 2 * kFeM * kFeLd;                    // [2][kFeN][kFeLd]
+  static_assert(kFeM * kFeOld * 4 <= kFeStages * kFeStage * 2, "epilogue tile fits");
+  __shared__ __attribute__((aligned(16))) uint16_t ring[kFeStages * kFeStage];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
@@ -80,61 +84,68 @@ __global__ __launch_bounds__(kFeThreads) void qkv_rope_kernel(FrontArgs a) {
   const int c0 = (nt % TPH) * 32;      // first pair index of the tile
   const int m0 = mt * kFeM;
 
-  // staged rows: X token rows (clamped past T: those results are dropped) and
-  // W feature rows (tile column j: the pair's first member for j < 32)
-  const uint16_t* xrow[kFePieces];
-  const uint16_t* wrow[kFePieces];
-  int pcol[kFePieces], prow[kFePieces];
+  // this lane's source row and piece for each of the wave's direct loads:
+  // staged row r < 64 is token m0 + r (clamped past T: those results are
+  // dropped), row 64 + j is the W row of tile feature j (the pair's first
+  // member for j < 32, its second for j >= 32)
+  const uint16_t* src[kFeLoads];
 #pragma unroll
-  for (int u = 0; u < kFePieces; ++u) {
-    const int p = tid + u * kFeThreads;
-    prow[u] = p / (kFeK / 8);
-    pcol[u] = (p % (kFeK / 8)) * 8;
-    const int t = min(m0 + prow[u], a.T - 1);
-    xrow[u] = a.x + (int64_t)t * a.hidden + pcol[u];
-    const int j = prow[u];
-    const int feat = hh * D + (j < 32 ? c0 + j : HALF + c0 + (j - 32));
-    wrow[u] = a.w + (int64_t)feat * a.hidden + pcol[u];
+  for (int u = 0; u < kFeLoads; ++u) {
+    const int r = (w * kFeLoads + u) * 8 + (lane >> 3);
+    const int c = fe_slot(r, lane & 7);  // the slot this lane fills holds piece c
+    if (r < kFeM) {
+      src[u] = a.x + (int64_t)min(m0 + r, a.T - 1) * a.hidden + c * 8;
+    } else {
+      const int j = r - kFeM;
+      const int feat = hh * D + (j < 32 ? c0 + j : HALF + c0 + (j - 32));
+      src[u] = a.w + (int64_t)feat * a.hidden + c * 8;
+    }
   }
-  u32x4 xr[kFePieces], wr[kFePieces];
-  auto load = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < kFePieces; ++u) {
-      xr[u] = *reinterpret_cast<const u32x4*>(xrow[u] + k0);
-      wr[u] = *reinterpret_cast<const u32x4*>(wrow[u] + k0);
-    }
-  };
-  auto store = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < kFePieces; ++u) {
-      *reinterpret_cast<u32x4*>(&xs[(buf * kFeM + prow[u]) * kFeLd + pcol[u]]) = xr[u];
-      *reinterpret_cast<u32x4*>(&ws[(buf * kFeN + prow[u]) * kFeLd + pcol[u]]) = wr[u];
-    }
-  };
-
   const int nchunks = a.hidden / kFeK;
-  load(0);
-  store(0);
-  __syncthreads();
+  auto issue = [&](int kc) __attribute__((always_inline)) {
+    uint16_t* stage = ring + (kc % kFeStages) * kFeStage;
+#pragma unroll
+    for (int u = 0; u < kFeLoads; ++u)
+      __builtin_amdgcn_global_load_lds(FE_GLOBAL(src[u] + kc * kFeK),
+                                       FE_LDS(stage + (w * kFeLoads + u) * 8 * kFeK), 16, 0, 0);
+  };
+#pragma unroll
+  for (int kc = 0; kc < kFeStages - 1; ++kc)
+    if (kc < nchunks) issue(kc);
+
+  // operand rows of this lane: token 32 wm + l32, feature 32 wn + l32
+  const int ra = 32 * wm + l32, rb = kFeM + 32 * wn + l32;
   f32x16 acc = {};
   for (int kc = 0; kc < nchunks; ++kc) {
-    const int cur = kc & 1;
-    const bool more = kc + 1 < nchunks;
-    if (more) load((kc + 1) * kFeK);
-    const uint16_t* xa = &xs[(cur * kFeM + 32 * wm + l32) * kFeLd + half * 8];
-    const uint16_t* wb = &ws[(cur * kFeN + 32 * wn + l32) * kFeLd + half * 8];
+    // chunk kc has landed once at most the later chunks' loads are in flight
+    const int later = min(nchunks - 1, kc + kFeStages - 2) - kc;
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(kWaitVm | (2 * kFeLoads));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(kWaitVm | kFeLoads);
+    else __builtin_amdgcn_s_waitcnt(kWaitVm);
+    // every wave's loads of chunk kc are in, and every wave is done with the
+    // stage the next load overwrites (no fence: later loads stay in flight)
+    __builtin_amdgcn_s_barrier();
+    if (kc + kFeStages - 1 < nchunks) issue(kc + kFeStages - 1);
+    const uint16_t* stage = ring + (kc % kFeStages) * kFeStage;
+    // every operand fragment of the chunk is read before its MFMAs
+    bf16x8 av[kFeK / 16], bv[kFeK / 16];
 #pragma unroll
     for (int kk = 0; kk < kFeK / 16; ++kk) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(xa + kk * 16);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(wb + kk * 16);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      const int c = 2 * kk + half;
+      av[kk] = *reinterpret_cast<const bf16x8*>(stage + ra * kFeK + fe_slot(ra, c) * 8);
+      bv[kk] = *reinterpret_cast<const bf16x8*>(stage + rb * kFeK + fe_slot(rb, c) * 8);
     }
-    if (more) store(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < kFeK / 16; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], bv[kk], acc, 0, 0, 0);
   }
+  static_assert(kFeStages - 2 <= 2, "the waits above cover at most two later chunks");
 
   // -- epilogue: tile[token][feature column] through LDS ----------------------
-  float* tile = reinterpret_cast<float*>(smem);
+  __builtin_amdgcn_s_waitcnt(kWaitVm);
+  __syncthreads();  // every operand read is done: the ring is free
+  float* tile = reinterpret_cast<float*>(ring);
   // lane holds feature column 32 wn + l32 and tokens 8(r/4) + 4 half + r%4
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -192,6 +203,7 @@ hipError_t launch_qkv_rope(const FrontArgs& a, int D, const Stream& st) {
   const int mtiles = (a.T + kFeM - 1) / kFeM;
   const int heads = a.Hq + 2 * a.Hkv;
   const dim3 grid((unsigned)(mtiles * heads * (D / 64)));
+  static_assert(kFeThreads == 256, "launch shape");
   if (D == 128)
     hipExtLaunchKernelGGL((qkv_rope_kernel<128>), grid, dim3(kFeThreads), 0, st.st, st.start,
                           st.stop, 0, a);

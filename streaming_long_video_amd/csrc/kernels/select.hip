@@ -45,6 +45,18 @@ __device__ inline uint32_t score_key(float x) {
   return u > 0x7F800000u ? 0u : u;  // NaN, -0 and negatives rank lowest
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads also makes each
+// wave's global stores visible first, i.e. waits for them to complete (the
+// importance row written right after the score sums would hold up the next
+// barrier by a memory round trip); nothing in the selecting workgroup reads
+// back global memory that another thread of it wrote, except the move lists
+// when they do not fit in LDS (that barrier stays a full one).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave-level primitives on DPP (every lane of the wave active).
 // Inclusive prefix sum over the 64 lanes: Hillis-Steele within each 16-lane
 // row (row_shr 1, 2, 4, 8, zero fill), then row 0 / 2 totals into rows 1 / 3
@@ -88,7 +100,7 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t v = wave_inclusive_sum(x);
   if (lane == 63) sh[w] = v;
-  __syncthreads();
+  lds_barrier();
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
@@ -96,7 +108,7 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh, uint32
     if (i < w) base += s;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   if (total) *total = tot;
   return base + v - x;
 }
@@ -108,14 +120,14 @@ __device__ inline uint32_t block_min_max(uint32_t mn, uint32_t mx, uint32_t* sh,
     sh[w] = mn;
     sh[kSelWaves + w] = mx;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t a = sh[0], b = sh[kSelWaves];
 #pragma unroll
   for (int i = 1; i < kSelWaves; ++i) {
     a = min(a, sh[i]);
     b = max(b, sh[kSelWaves + i]);
   }
-  __syncthreads();
+  lds_barrier();
   *out_max = b;
   return a;
 }
@@ -189,7 +201,7 @@ __device__ void apply_moves(const InPlace& ip, const int32_t* mv, int M, int h0,
 }
 
 struct SumJob {
-  const f32x4* part;      // [S][n4]
+  const f32x4* part;      // [S][n4] split partials (already unscaled)
   void* out;              // [n4] f32x4, or [n4] x 4 bf16 when bf16
   int64_t n4;
   int S;
@@ -200,12 +212,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 __device__ void select_one_head(const SelectJob& J, int h) {
   extern __shared__ uint32_t keys[];
-  // per-wave digit histograms, two 16-bit counters per word (a wave sees at
-  // most kMaxPool / kSelWaves = 2048 keys)
-  __shared__ uint32_t whist[2][kSelWaves][128];
+  // one digit histogram of 12-bit digits for the whole workgroup
+  constexpr int kDigitBits = 12;
+  constexpr int kBins = 1 << kDigitBits;
+  constexpr int kBinsPerThread = kBins / kSelThreads;
+  static_assert(kBinsPerThread * kSelThreads == kBins, "bins split evenly");
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t red[2 * kSelWaves];
-  __shared__ uint32_t wtot[4];
-  __shared__ uint32_t found[2][3];
+  __shared__ uint32_t found[3];
   const int tid = threadIdx.x, w = tid >> 6;
   const int pool = J.pool, budget = J.budget;
   const float* sp = J.sig_part + (int64_t)h * J.rt * J.ldsig;
@@ -287,18 +301,19 @@ __device__ void select_one_head(const SelectJob& J, int h) {
       mx = max(mx, u);
     }
   }
-  // the first pass's histogram starts cleared (the min/max barrier orders it)
-  for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[0][0][0])[i] = 0u;
+  // the histogram starts cleared (the min/max barrier orders the clears)
+  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0u;
   uint32_t kmax;
   uint32_t kmin = block_min_max(mn, mx, red, &kmax);  // also orders keys[] writes
 
   const int lane = tid & 63;
-  int buf = 0;  // whist[buf] is clear whenever a radix select starts
   uint32_t prefix, pmask, k;
-  // radix select below the common prefix of all keys; histograms and the
-  // boundary record alternate between two buffers so that a pass needs three
-  // barriers.  Returns the boundary bin's size; k is then the number of its
-  // keys to keep.
+  // MSB-first radix select below the common prefix of all keys, 12-bit
+  // digits.  Per pass: count the keys that match the prefix by digit; thread
+  // tid owns the digits dmask - 4 tid - e (e < 4, highest first), reads and
+  // clears them (so every bin is zero again when the pass ends) and a
+  // workgroup scan of the owners' sums finds the boundary digit.  Returns the
+  // boundary bin's size; k is then the number of its keys to keep.
   auto radix = [&]() -> uint32_t {
     prefix = kmin;
     pmask = 0xFFFFFFFFu;
@@ -310,49 +325,45 @@ __device__ void select_one_head(const SelectJob& J, int h) {
     }
     uint32_t bin = (uint32_t)pool;
     while (hb >= 0) {
-      const int shift = hb >= 7 ? hb - 7 : 0;
+      const int shift = hb >= kDigitBits - 1 ? hb - (kDigitBits - 1) : 0;
       const uint32_t dmask = (2u << (hb - shift)) - 1u;  // digit bits [shift, hb]
       for (int j = tid; j < pool; j += kSelThreads) {
         const uint32_t u = keys[j];
-        if ((u & pmask) == prefix) {
-          const uint32_t dig = (u >> shift) & dmask;
-          atomicAdd(&whist[buf][w][dig >> 1], 1u << ((dig & 1u) * 16u));
-        }
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & dmask], 1u);
       }
-      for (int i = tid; i < kSelWaves * 128; i += kSelThreads) (&whist[buf ^ 1][0][0])[i] = 0u;
-      __syncthreads();
-      // digits in descending order over threads 0..255 (waves 0..3)
-      const uint32_t d = 255u - (uint32_t)tid;
-      uint32_t cnt = 0, incl = 0;
-      if (tid < 256) {
-        if (d <= dmask) {
+      lds_barrier();
+      uint32_t cnt[kBinsPerThread], tsum = 0;
 #pragma unroll
-          for (int i = 0; i < kSelWaves; ++i) cnt += (whist[buf][i][d >> 1] >> ((d & 1u) * 16u)) & 0xFFFFu;
+      for (int e = 0; e < kBinsPerThread; ++e) {
+        const int d = (int)dmask - kBinsPerThread * tid - e;
+        cnt[e] = 0;
+        if (d >= 0) {
+          cnt[e] = hist[d];
+          hist[d] = 0u;
         }
-        incl = wave_inclusive_sum(cnt);
-        if (lane == 63) wtot[w] = incl;
+        tsum += cnt[e];
       }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t excl = incl - cnt;
-        for (int i = 0; i < w; ++i) excl += wtot[i];
-        if (cnt && excl < k && k <= excl + cnt) {
-          found[buf][0] = d;
-          found[buf][1] = excl;
-          found[buf][2] = cnt;
+      const uint32_t incl = wave_inclusive_sum(tsum);
+      if (lane == 63) red[w] = incl;
+      lds_barrier();
+      uint32_t excl = incl - tsum;
+      for (int i = 0; i < w; ++i) excl += red[i];
+#pragma unroll
+      for (int e = 0; e < kBinsPerThread; ++e) {
+        if (cnt[e] && excl < k && k <= excl + cnt[e]) {
+          found[0] = dmask - (uint32_t)(kBinsPerThread * tid + e);
+          found[1] = excl;
+          found[2] = cnt[e];
         }
+        excl += cnt[e];
       }
-      __syncthreads();
-      prefix |= found[buf][0] << shift;
+      lds_barrier();
+      prefix |= found[0] << shift;
       pmask |= dmask << shift;
-      k -= found[buf][1];
-      bin = found[buf][2];
-      if (bin == k) {  // the whole boundary bin is kept: no tie to break
-        buf ^= 1;  // whist[buf ^ 1] was cleared during this pass
-        break;
-      }
+      k -= found[1];
+      bin = found[2];
+      if (bin == k) break;  // the whole boundary bin is kept: no tie to break
       hb = shift - 1;
-      buf ^= 1;
     }
     return bin;
   };
@@ -376,14 +387,21 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   // keep (u & pmask) > prefix, and the first k keys with (u & pmask) == prefix
   const int per = (pool + kSelThreads - 1) / kSelThreads;
   const int j0 = min(pool, tid * per), j1 = min(pool, j0 + per);
-  uint32_t ngt = 0u, neq = 0u;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t u = keys[j] & pmask;
-    ngt += u > prefix;
-    neq += u == prefix;
+  // ranks among the keys above / at the boundary before this thread's range:
+  // in place, only needed when the boundary bin is kept in part (otherwise
+  // every boundary key is kept and ranks do not matter)
+  uint32_t gt_before = 0u, eq_before = 0u;
+  if (!in_place || bin != k) {
+    uint32_t ngt = 0u, neq = 0u;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t u = keys[j] & pmask;
+      ngt += u > prefix;
+      neq += u == prefix;
+    }
+    const uint32_t packed = block_exclusive_scan(ngt | (neq << 16), red, nullptr);
+    gt_before = packed & 0xFFFFu;
+    eq_before = packed >> 16;
   }
-  const uint32_t packed = block_exclusive_scan(ngt | (neq << 16), red, nullptr);
-  const uint32_t gt_before = packed & 0xFFFFu, eq_before = packed >> 16;
   if (!in_place) {
     uint32_t slot = gt_before + min(eq_before, k);
     uint32_t eqr = eq_before;
@@ -432,8 +450,11 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   const int M = min((int)(tot >> 16), T);
   if (tid == 0) out[2 * T] = M;
   // the lists are read back by other threads of this workgroup: the barrier
-  // makes the writes above visible to them
-  __syncthreads();
+  // makes the writes above visible to them (global lists need the full one)
+  if (lists_lds)
+    lds_barrier();
+  else
+    __syncthreads();
   apply_moves(J.ip, lst, M, mh0, mh1);
 }
 
@@ -497,9 +518,18 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
   const int64_t nb = gridDim.x - n_select;
   for (int64_t i = (int64_t)(blockIdx.x - n_select) * kSelThreads + threadIdx.x; i < Sj.n4;
        i += nb * kSelThreads) {
-    f32x4 acc = Sj.part[i];
-    for (int s = 1; s < Sj.S; ++s) acc += Sj.part[s * Sj.n4 + i];
-    acc *= kOPartUnscale;
+    // every split's load in flight, then the sum in split order
+    constexpr int kMaxSplitsInFlight = 16;
+    f32x4 pv[kMaxSplitsInFlight];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < Sj.S; s0 += kMaxSplitsInFlight) {
+#pragma unroll
+      for (int u = 0; u < kMaxSplitsInFlight; ++u)
+        if (s0 + u < Sj.S) pv[u] = Sj.part[(s0 + u) * Sj.n4 + i];
+#pragma unroll
+      for (int u = 0; u < kMaxSplitsInFlight; ++u)
+        if (s0 + u < Sj.S) acc += pv[u];
+    }
     if (Sj.bf16)
       static_cast<bf16x4*>(Sj.out)[i] = __builtin_convertvector(acc, bf16x4);
     else
@@ -537,17 +567,14 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
   SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0};
-  // The O sum runs beside the selection, which is the launch's long pole:
-  // few workgroups with several outputs per thread leave the selecting
-  // workgroups more of the memory system, as long as the sum still ends
-  // first.  Measured at the 8B-like shape: 3.5 f32x4 outputs per thread (64
-  // workgroups) when the selecting workgroups also move rows in place, 1.75
-  // (128) otherwise, each 1.5-2 us faster than one output per thread.
+  // The O sum runs beside the selection: enough workgroups that it ends
+  // before the selection (two f32x4 outputs per thread, reading S partials
+  // each), few enough to leave the selecting workgroups most of the memory
+  // system.
   int sum_blocks = 0;
   if (o_part && S > 1 && o_elems > 0) {
-    const int64_t per2 = ip.pos ? 7 : 4;  // twice the outputs per thread, rounded
-    const int64_t want = (2 * Sj.n4 + per2 * kSelThreads - 1) / (per2 * kSelThreads);
-    sum_blocks = (int)(want < 64 ? 64 : want > 1024 ? 1024 : want);
+    const int64_t want = (Sj.n4 + 2 * kSelThreads - 1) / (2 * kSelThreads);
+    sum_blocks = (int)(want < 32 ? 32 : want > 1024 ? 1024 : want);
   }
   AppendJob A = {};
   int n_append = 0;

@@ -88,13 +88,13 @@ struct AppendJob {
   int T, Hkv, D, ring;
 };
 hipError_t launch_attn_out(const AttnArgs& a, int D, const Stream& st);
-// The output pass forms P scaled by 2^12 (fp16 range); its split O partials
-// keep that scale, and the sum of the splits removes it (exactly: a power of 2).
+// The output pass forms P scaled by 2^12 (fp16 range) and removes the scale
+// (exactly: a power of 2) before it writes O or its split partials.
 constexpr float kOPartUnscale = 1.f / 4096.f;
 // One launch: per KV head, sums the score partials (scores may be null),
 // selects the top-B or keeps all (sel); concurrently, when o_part is given
-// and S > 1, o[i] = kOPartUnscale * sum_{s<S} o_part[s*o_elems + i] in split
-// order (o fp32, or bf16 rounded to nearest even when o_bf16).
+// and S > 1, o[i] = sum_{s<S} o_part[s*o_elems + i] in split order (o fp32,
+// or bf16 rounded to nearest even when o_bf16).
 // Standalone mode: rt = 1 and sig_part holds the scores.  In place (ip.pos
 // set), each selection row holds the rows to refill at [0, T), the kept frame
 // tokens at [T, 2T) and their count at 2T, and the launch applies the moves;
