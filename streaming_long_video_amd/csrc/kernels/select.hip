@@ -568,12 +568,14 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
   SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0};
   // The O sum runs beside the selection: enough workgroups that it ends
-  // before the selection (two f32x4 outputs per thread, reading S partials
-  // each), few enough to leave the selecting workgroups most of the memory
+  // before the selection (about 18 partial loads per thread: two f32x4
+  // outputs of 9 splits at the 8B-like shape, one output when there are more
+  // splits), few enough to leave the selecting workgroups most of the memory
   // system.
   int sum_blocks = 0;
   if (o_part && S > 1 && o_elems > 0) {
-    const int64_t want = (Sj.n4 + 2 * kSelThreads - 1) / (2 * kSelThreads);
+    const int64_t per_thread = S >= 18 ? 1 : 18 / S;
+    const int64_t want = (Sj.n4 + per_thread * kSelThreads - 1) / (per_thread * kSelThreads);
     sum_blocks = (int)(want < 32 ? 32 : want > 1024 ? 1024 : want);
   }
   AppendJob A = {};

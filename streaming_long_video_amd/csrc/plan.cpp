@@ -62,7 +62,14 @@ int make_plan(const statekv_layer_config* cfg, Plan* p) {
   q.max_tiles = ceil_div(q.max_pool, kKeyTile);
   const int per_split = Hkv * q.rt;
   int s = cfg->num_splits;
-  if (s == 0) s = per_split >= kTargetWGs ? 1 : kTargetWGs / per_split;
+  if (s == 0) {
+    // one workgroup per CU, but at least kMinTilesPerSplit key tiles per
+    // split: each split costs a fixed prologue and epilogue and one O partial
+    // of T*Hq*d floats, which small pools cannot amortise
+    s = per_split >= kTargetWGs ? 1 : kTargetWGs / per_split;
+    const int by_tiles = q.max_tiles / kMinTilesPerSplit;
+    if (s > by_tiles) s = by_tiles;
+  }
   if (s > q.max_tiles) s = q.max_tiles;
   if (s < 1) s = 1;
   q.splits = s;

@@ -41,6 +41,8 @@ KERNELS = {
     "full_attn": r"attn_kernel<128, 3(, false)?>",
     "full_combine": r"full_combine_kernel<128>",
     "decode": r"decode_kernel<128>",
+    "decode_merge": r"decode_merge_kernel<128>",
+    "qkv_rope": r"qkv_rope_kernel<128>",
 }
 PROBE = r"neg"  # torch's negation kernel: the copy probe
 
@@ -78,7 +80,7 @@ def _one(pattern: str, root: str) -> str:
 
 
 def _short(name: str) -> str:
-    name = name.replace("void ", "")
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
     return name.split("(")[0]
 
 
