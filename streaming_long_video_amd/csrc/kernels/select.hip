@@ -10,10 +10,12 @@
 // Scores are non-negative fp32, so their bit patterns order like the values
 // (NaN and negative patterns are mapped to 0).  The threshold is found by an
 // MSB-first radix select over the bits below the highest bit in which the
-// pool's keys differ (so the first 8-bit digit already spreads the keys over
-// the histogram), with one histogram per wave to keep LDS atomics on distinct
-// addresses.  After each digit, if every key of the boundary bin is needed the
-// search stops early.  The kept set is every key above the boundary plus the
+// pool's keys differ (so the first 12-bit digit already spreads the keys over
+// the histogram), with one 4096-bin LDS histogram per digit: each thread
+// owns four bins, reads and clears them after the counting, and one
+// workgroup scan over the bins finds the boundary bin (three barriers per
+// digit; at most three digits).  After each digit, if every key of the
+// boundary bin is needed the search stops early.  The kept set is every key above the boundary plus the
 // first k keys of the boundary bin in pool order, compacted with one
 // workgroup scan so the output lists pool indices in ascending order.  Only
 // integer operations decide the result: exact and deterministic.
@@ -35,7 +37,6 @@ namespace skv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-static_assert(kMaxPool / kSelWaves < 65536, "16-bit per-wave histogram counters");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
