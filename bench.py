@@ -638,13 +638,19 @@ def run_frontend(args):
             torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev),
             torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=dev))
     L = len(ws)
+    need = skv.qkv_rope_workspace_bytes(T, hid, Hq, Hkv, d)
+    work = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
     for i in range(args.warmup + L):
-        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs)
+        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs,
+                     workspace=work)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
+    t0 = time.perf_counter()
     for i in range(args.steps):
-        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs)
+        skv.qkv_rope(xs[i % 8], ws[i % L], Hq, Hkv, d, i * T, spec.rope_theta, out=outs,
+                     workspace=work)
+    host_us = (time.perf_counter() - t0) * 1e6 / args.steps
     ev[1].record()
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
@@ -654,7 +660,8 @@ def run_frontend(args):
     print(json.dumps({
         "mode": "frontend", "workload": args.workload, "tokens": T, "hidden": hid,
         "out_features": rows, "weight_copies": L, "calls": args.steps,
-        "us_per_call": us, "algorithmic_bytes": nbytes,
+        "us_per_call": us, "host_us_per_call": host_us, "workspace_bytes": need,
+        "algorithmic_bytes": nbytes,
         "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
         "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "gflop": flops / 1e9, "tflops": flops / (us * 1e-6) / 1e12,

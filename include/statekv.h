@@ -265,17 +265,35 @@ int statekv_rope(statekv_layer* layer, void* x, int32_t n_tokens, int32_t n_head
  *   token t sits at position first_position + t; rope_theta > 0 rotates q and
  *   k (pairs (x_i, x_{i+d/2}), angle (p / rope_scaling) * rope_theta^(-2i/d),
  *   rope_scaling <= 0 means 1); rope_theta = 0 leaves them unrotated.
- * Arithmetic: fp32 accumulation of the bf16 products, the rotation in double
- * from the fp32 sums, one rounding to bf16 (nearest, ties to even).
+ * Arithmetic: fp32 accumulation of the bf16 products (in up to a few splits
+ * of the hidden dimension, summed in split order: deterministic), the
+ * rotation in double from the fp32 sums, one rounding to bf16 (nearest, ties
+ * to even).
+ * workspace: device, 256-byte aligned, at least the bytes that
+ *   statekv_qkv_rope_workspace_size gives for these sizes (the splits' fp32
+ *   partial sums); owned by the caller, not read across calls, and must not
+ *   be in use by another call in flight.  NULL (workspace_bytes ignored): the
+ *   library takes the bytes it needs, if any, with hipMallocAsync on `stream`
+ *   and frees them with hipFreeAsync on `stream` after the last kernel.
  * Errors (host checks, nothing enqueued): STATEKV_ERR_INVALID_ARGUMENT for a
  * null or misaligned pointer, a non-positive size, Hq not a multiple of Hkv,
  * a negative first_position, rope_theta < 0, = 1 or not finite;
  * STATEKV_ERR_UNSUPPORTED for d other than 64/128, hidden not a multiple of
- * 64, or sizes beyond 2^20 tokens or features.  Asynchronous on stream. */
+ * 64, or sizes beyond 2^20 tokens or features; STATEKV_ERR_WORKSPACE for a
+ * workspace that is misaligned or smaller than needed; STATEKV_ERR_HIP if a
+ * launch or the stream-ordered allocation fails.  Asynchronous on stream. */
 int statekv_qkv_rope(const void* x, const void* w, int32_t n_tokens, int32_t hidden,
                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                      int64_t first_position, double rope_theta, double rope_scaling,
-                     void* q, void* k, void* v, void* stream);
+                     void* q, void* k, void* v, void* workspace, uint64_t workspace_bytes,
+                     void* stream);
+
+/* Bytes of the workspace statekv_qkv_rope needs for these sizes (0 if it does
+ * not split the hidden dimension), written to *bytes.  Host only; the same
+ * size errors as statekv_qkv_rope (STATEKV_ERR_INVALID_ARGUMENT /
+ * _UNSUPPORTED), STATEKV_ERR_INVALID_ARGUMENT for a null `bytes`. */
+int statekv_qkv_rope_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_q_heads,
+                                    int32_t n_kv_heads, int32_t head_dim, uint64_t* bytes);
 
 /* Views (host only; they enqueue nothing and never fail on a valid layer;
  * STATEKV_ERR_INVALID_ARGUMENT for a null argument).

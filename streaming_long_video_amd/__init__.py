@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     statekv_profile_start,
     statekv_profile_stop,
     statekv_qkv_rope,
+    statekv_qkv_rope_workspace_size,
     statekv_reset_layer,
     statekv_restore_layer,
     statekv_rope,
@@ -39,6 +40,6 @@ from ._binding import (  # noqa: F401
     statekv_status_string,
     statekv_workspace_bytes,
 )
-from .layer import Layer, qkv_rope, select_topb  # noqa: F401
+from .layer import Layer, qkv_rope, qkv_rope_workspace_bytes, select_topb  # noqa: F401
 
 load_library()

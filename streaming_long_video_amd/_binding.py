@@ -116,7 +116,10 @@ def load_library() -> ctypes.CDLL:
         "statekv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, P]),
         "statekv_qkv_rope": (ctypes.c_int, [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                            ctypes.c_double, ctypes.c_double, P, P, P, P]),
+                                            ctypes.c_double, ctypes.c_double, P, P, P, P,
+                                            ctypes.c_uint64, P]),
+        "statekv_qkv_rope_workspace_size": (ctypes.c_int, [ctypes.c_int32] * 5
+                                            + [ctypes.POINTER(ctypes.c_uint64)]),
         "statekv_state": (ctypes.c_int, [P, ctypes.POINTER(statekv_state_view)]),
         "statekv_detailed_cache": (ctypes.c_int, [P, ctypes.POINTER(statekv_cache_view)]),
         "statekv_reset_layer": (ctypes.c_int, [P]),
@@ -206,10 +209,21 @@ def statekv_rope(layer: int, x: int, n_tokens: int, n_heads: int, first_position
 
 def statekv_qkv_rope(x: int, w: int, n_tokens: int, hidden: int, n_q_heads: int,
                      n_kv_heads: int, head_dim: int, first_position: int, rope_theta: float,
-                     rope_scaling: float, q: int, k: int, v: int, stream: int = 0) -> None:
+                     rope_scaling: float, q: int, k: int, v: int, workspace: int = 0,
+                     workspace_bytes: int = 0, stream: int = 0) -> None:
     _check(load_library().statekv_qkv_rope(x, w, n_tokens, hidden, n_q_heads, n_kv_heads,
                                            head_dim, first_position, rope_theta, rope_scaling,
-                                           q, k, v, stream or None), "statekv_qkv_rope")
+                                           q, k, v, workspace or None, workspace_bytes,
+                                           stream or None), "statekv_qkv_rope")
+
+
+def statekv_qkv_rope_workspace_size(n_tokens: int, hidden: int, n_q_heads: int,
+                                    n_kv_heads: int, head_dim: int) -> int:
+    n = ctypes.c_uint64()
+    _check(load_library().statekv_qkv_rope_workspace_size(n_tokens, hidden, n_q_heads,
+                                                          n_kv_heads, head_dim, ctypes.byref(n)),
+           "statekv_qkv_rope_workspace_size")
+    return n.value
 
 
 def statekv_state(layer: int) -> statekv_state_view:

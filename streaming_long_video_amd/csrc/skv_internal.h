@@ -5,6 +5,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "plan.h"
@@ -184,7 +185,15 @@ struct FrontArgs {
   int T, hidden, Hq, Hkv;
   int64_t first_position;  // position of token 0
   double theta, scaling;   // theta <= 0: no rotation
+  double inv_freq[64];     // theta^(-2i/D) for pair index i < D/2 (host-computed)
+  int S;                   // splits of the hidden dimension
+  float* part;             // S > 1: [S][feature tiles][T][128] fp32 partial sums
+  double* rot;             // S > 1: [T][D/2] (cos, sin) of each token's angle per pair index
 };
+// splits of the hidden dimension the front end uses, and the bytes of its
+// partial sums (0 when it does not split)
+int qkv_rope_splits(int T, int hidden, int heads, int D);
+size_t qkv_rope_workspace_bytes(int T, int hidden, int heads, int D);
 hipError_t launch_qkv_rope(const FrontArgs& a, int D, const Stream& st);
 
 // App. A diagnostics of the last frame (one workgroup per budget).

@@ -212,10 +212,13 @@ class Layer:
 
 def qkv_rope(x: torch.Tensor, w: torch.Tensor, n_q_heads: int, n_kv_heads: int, head_dim: int,
              first_position: int, rope_theta: float, rope_scaling: float = 0.0,
-             out=None, stream=None):
+             out=None, workspace=None, stream=None):
     """The library's frame front end: q, k, v = rope(X W_Q), rope(X W_K), X W_V.
     x: [T][hidden] bf16; w: [(Hq + 2 Hkv) d][hidden] bf16 (output-major, rows
-    Q heads, K heads, V heads).  Returns (q, k, v) bf16 [T][H][d] tensors."""
+    Q heads, K heads, V heads).  Returns (q, k, v) bf16 [T][H][d] tensors.
+    workspace: a uint8 device tensor of at least
+    qkv_rope_workspace_bytes(...) bytes for the hidden-dimension splits' partial
+    sums; taken from torch's allocator when None."""
     T, hidden = x.shape
     rows = (n_q_heads + 2 * n_kv_heads) * head_dim
     for name, t, shape in (("x", x, (T, hidden)), ("w", w, (rows, hidden))):
@@ -228,10 +231,24 @@ def qkv_rope(x: torch.Tensor, w: torch.Tensor, n_q_heads: int, n_kv_heads: int, 
                torch.empty((T, n_kv_heads, head_dim), dtype=torch.bfloat16, device=x.device),
                torch.empty((T, n_kv_heads, head_dim), dtype=torch.bfloat16, device=x.device))
     q, k, v = out
+    if workspace is None:
+        need = B.statekv_qkv_rope_workspace_size(T, hidden, n_q_heads, n_kv_heads, head_dim)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            if stream is not None:
+                workspace.record_stream(stream)  # not reused before the launch stream passes it
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     B.statekv_qkv_rope(x.data_ptr(), w.data_ptr(), T, hidden, n_q_heads, n_kv_heads, head_dim,
                        int(first_position), float(rope_theta), float(rope_scaling),
-                       q.data_ptr(), k.data_ptr(), v.data_ptr(), _stream_ptr(stream))
+                       q.data_ptr(), k.data_ptr(), v.data_ptr(), ws_ptr, ws_bytes,
+                       _stream_ptr(stream))
     return q, k, v
+
+
+def qkv_rope_workspace_bytes(T: int, hidden: int, n_q_heads: int, n_kv_heads: int,
+                             head_dim: int) -> int:
+    """Bytes of the front end's workspace for these sizes (0: it does not split)."""
+    return B.statekv_qkv_rope_workspace_size(T, hidden, n_q_heads, n_kv_heads, head_dim)
 
 
 def select_topb(scores: torch.Tensor, budget: int, stream=None) -> torch.Tensor:

@@ -250,6 +250,35 @@ def test_front_end_argument_errors_are_host_side():
         with pytest.raises(B.StateKVError) as e:
             B.statekv_qkv_rope(**args)
         assert e.value.status == status, change
+    # a caller's workspace that is too small or not 256-byte aligned
+    need = B.statekv_qkv_rope_workspace_size(256, 3584, 28, 4, 128)
+    for change in (dict(workspace=a, workspace_bytes=need - 1),
+                   dict(workspace=a + 16, workspace_bytes=need)):
+        with pytest.raises(B.StateKVError) as e:
+            B.statekv_qkv_rope(**dict(good, **change))
+        assert e.value.status == -3, change
+
+
+def test_front_end_workspace_size():
+    """The splits' partial sums (S x feature tiles x T x 128 fp32) and the
+    rotation table (T x d/2 (cos, sin) doubles), with S chosen so the
+    tiles x S workgroups fit one per CU, each split covers at least 8 chunks
+    of 64 hidden features and S <= 8; no workspace without a split."""
+    size = B.statekv_qkv_rope_workspace_size
+    # 8B shape: 2 token tiles x 36 heads = 72 tiles, S = min(256 // 72, 56 // 8) = 3
+    assert size(256, 3584, 28, 4, 128) == 3 * 36 * 256 * 128 * 4 + 256 * 64 * 16
+    # ragged T = 100: one token tile, S = min(256 // 36, 7) = 7
+    assert size(100, 3584, 28, 4, 128) == 7 * 36 * 100 * 128 * 4 + 100 * 64 * 16
+    # many chunks, few tiles: S capped at 8
+    assert size(64, 8192, 4, 2, 64) == 8 * 4 * 64 * 128 * 4 + 64 * 32 * 16
+    # 1B shape: hidden 896 is 14 chunks, too few to split
+    assert size(256, 896, 14, 2, 64) == 0
+    assert size(16, 128, 2, 1, 64) == 0
+    for args, status in (((0, 3584, 28, 4, 128), -1), ((256, 3584, 27, 4, 128), -1),
+                         ((256, 3584, 28, 4, 96), -2), ((256, 3600, 28, 4, 128), -2)):
+        with pytest.raises(B.StateKVError) as e:
+            size(*args)
+        assert e.value.status == status, args
 
 
 def test_status_strings():
