@@ -36,7 +36,8 @@
  *   - `stream` is a hipStream_t (NULL = default stream).  Work is enqueued
  *     asynchronously; results are ready once the stream is synchronised.
  *   - The caller owns every device buffer, including the one workspace; the
- *     library never allocates device memory.  The layer handle is host memory
+ *     library allocates no device memory, except statekv_qkv_rope when called
+ *     without a workspace (stream-ordered, freed on the same stream).  The layer handle is host memory
  *     owned by the library until statekv_free_layer.
  *   - Every argument check is done on the host before anything is enqueued; on
  *     an error return other than STATEKV_ERR_HIP nothing was enqueued and the
