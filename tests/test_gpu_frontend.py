@@ -112,3 +112,34 @@ def test_front_end_feeds_the_prefill_step():
         r = teacher_forced_frame(orc, layer, n, to_bits(q), to_bits(k), to_bits(v))
         print(f"frame {n}: relrms {r.relrms:.2e} kept {r.kept_match}/{r.kept_total}")
         assert r.relrms <= 1e-3 and r.maxabs <= 2e-2 and r.score_err <= 1.0
+
+
+def test_front_end_workspace_forms_agree():
+    """statekv_qkv_rope through the C ABI with the caller's workspace and
+    with none (the library's stream-ordered allocation): bit-identical q, k,
+    v at the 8B shape (split hidden dimension) and the 1B shape (no split,
+    no workspace needed), on two calls in a row."""
+    from streaming_long_video_amd import _binding as B
+
+    for name in ("internvl3_8b_layer", "internvl3_1b_layer"):
+        spec = framegen.workload(name)
+        Hq, Hkv, d, T = spec.n_q_heads, spec.n_kv_heads, spec.head_dim, spec.frame_tokens
+        x = to_dev(framegen.hidden_states(spec, 9))
+        w = to_dev(framegen.projection_weights(spec))
+        hidden = x.shape[1]
+        need = B.statekv_qkv_rope_workspace_size(T, hidden, Hq, Hkv, d)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        print(f"{name}: workspace {need} bytes", flush=True)
+        outs = []
+        for workspace, nbytes in ((ws.data_ptr(), need), (0, 0), (ws.data_ptr(), need), (0, 0)):
+            q = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=x.device)
+            k = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=x.device)
+            v = torch.empty((T, Hkv, d), dtype=torch.bfloat16, device=x.device)
+            B.statekv_qkv_rope(x.data_ptr(), w.data_ptr(), T, hidden, Hq, Hkv, d, 9 * T,
+                               spec.rope_theta, 0.0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               workspace, nbytes, 0)
+            outs.append((q, k, v))
+        torch.cuda.synchronize()
+        for other in outs[1:]:
+            for a, b in zip(outs[0], other):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
