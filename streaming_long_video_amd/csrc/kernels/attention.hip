@@ -407,10 +407,12 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
   }
   if constexpr (PASS == 2) {
     // Row log-sum-exp (base 2, scaled logits) of the row tile's 256 rows from
-    // the statistics pass's per-split (max, sum) pairs.  Thread pair
-    // (r, r + 256) takes row r, each half of the splits (even / odd index),
-    // every load of a group in flight at once; the halves merge through LDS.
-    // 12 is subtracted so that P comes out * 2^12.
+    // the statistics pass's per-split log-sum-exps (one float per row and
+    // split: half the bytes of a (max, sum) pair, and this prologue's loads
+    // are what it waits for).  Thread pair (r, r + 256) takes row r, each
+    // half of the splits (even / odd index), every load of a group in flight
+    // at once; the halves merge through LDS.  12 is subtracted so that P
+    // comes out * 2^12.
     {
       static_assert(kThreads == 2 * kRowBlk * kTokBlk, "two threads per row");
       constexpr int kGrp = 16;
@@ -427,8 +429,9 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
         // conditional; exp2 of -inf (an empty split) is 0
         const int stride = a.Hq * a.tpad, last = a.Sst - 1;
         const uint32_t rbytes = (uint32_t)((h * a.G + b % a.G) * a.tpad + t) * 4u;
+        // M: the largest split log-sum-exp so far, L: sum of 2^(lse - M)
         for (int s0 = par; s0 < a.Sst; s0 += 2 * kGrp) {
-          float mv[kGrp], lv[kGrp];
+          float mv[kGrp];
 #pragma unroll
           for (int u = 0; u < kGrp; ++u) {
             const int sp = s0 + 2 * u;
@@ -436,18 +439,15 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
             // scalar base + 32-bit lane offset: one address register for all loads
             const float mr = *reinterpret_cast<const float*>(
                 reinterpret_cast<const char*>(a.m_part + o) + rbytes);
-            const float lr = *reinterpret_cast<const float*>(
-                reinterpret_cast<const char*>(a.l_part + o) + rbytes);
             mv[u] = sp <= last ? mr : -INFINITY;
-            lv[u] = sp <= last ? lr : 0.f;
           }
           float Mg = M;
 #pragma unroll
           for (int u = 0; u < kGrp; ++u) Mg = fmaxf(Mg, mv[u]);
           const float Ms = Mg == -INFINITY ? 0.f : Mg;
-          L = L * __builtin_amdgcn_exp2f((M - Ms) * sl2);
+          L = L * __builtin_amdgcn_exp2f(M - Ms);
 #pragma unroll
-          for (int u = 0; u < kGrp; ++u) L += lv[u] * __builtin_amdgcn_exp2f((mv[u] - Ms) * sl2);
+          for (int u = 0; u < kGrp; ++u) L += __builtin_amdgcn_exp2f(mv[u] - Ms);
           M = Mg;
         }
       }
@@ -461,9 +461,9 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
         const float m0 = mh[0][rr], m1 = mh[1][rr];
         const float Mx = fmaxf(m0, m1);
         float Lx = 0.f;
-        if (m0 > -INFINITY) Lx += lh[0][rr] * exp2f((m0 - Mx) * sl2);
-        if (m1 > -INFINITY) Lx += lh[1][rr] * exp2f((m1 - Mx) * sl2);
-        lse2[i] = Mx * sl2 + log2f(Lx) - 12.f;
+        if (m0 > -INFINITY) Lx += lh[0][rr] * exp2f(m0 - Mx);
+        if (m1 > -INFINITY) Lx += lh[1][rr] * exp2f(m1 - Mx);
+        lse2[i] = Mx + log2f(Lx) - 12.f;
       }
     }
   }
@@ -843,9 +843,10 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
       if (mrun[i] > -INFINITY) L += lrun[i] * exp2f((mrun[i] - M) * sl2);
       if (mo > -INFINITY) L += lo * exp2f((mo - M) * sl2);
       if (half == 0 && qtok[i] >= 0) {
+        // the split's log-sum-exp (base 2, scaled logits); -inf: no key of
+        // the split is visible to the row
         const int64_t idx = ((int64_t)s * a.Hq + qhead[i]) * a.tpad + qtok[i];
-        a.m_part[idx] = M;
-        a.l_part[idx] = L;
+        a.m_part[idx] = L > 0.f ? M * sl2 + log2f(L) : -INFINITY;
       }
     }
   }

@@ -41,8 +41,10 @@ struct AttnArgs {
   const uint16_t* vf;  // [T][Hkv][D] bf16, frame values
   const uint16_t* kc;  // [Hkv][ldc][D] bf16, state keys (rows [0, c) live)
   const uint16_t* vc;  // [Hkv][ldc][D] bf16, state values
-  float* m_part;       // [Sst][Hq][tpad] per-split row max of raw logits
-  float* l_part;       // [Sst][Hq][tpad] per-split sum of exp relative to m
+  float* m_part;       // statistics pass: [Sst][Hq][tpad] per-split row log-sum-exp of the
+                       // logits scaled by scale_log2 (base 2); full attention: [S][Hq][tpad]
+                       // per-split row max of raw logits
+  float* l_part;       // full attention: [S][Hq][tpad] per-split sum of exp relative to m
   float* o_out;        // [T][Hq][D] fp32 when S == 1, else [S][T][Hq][D] partials
   int out_bf16;        // S == 1: o_out holds [T][Hq][D] bf16 instead
   float* sig_part;     // [Hkv][rt][ldsig] per-row-tile score partials
