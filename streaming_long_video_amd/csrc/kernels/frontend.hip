@@ -32,12 +32,15 @@
 //
 // 128 x 128 tiles leave few workgroups (72 at the 8B shape), so the hidden
 // dimension is split S ways (216 workgroups, one per CU).  With S = 1 the
-// GEMM kernel rotates and rounds its own tile; otherwise it stores fp32
-// partial tiles and qkv_combine_kernel sums the S partials of each output in
-// split order (deterministic), rotates and rounds.  Rotation is in fp64 with
-// an angle recurrence over consecutive tokens; each output is rounded to bf16
-// once.  Workgroup ids are renumbered so the token tiles of one (feature
-// tile, split) run on the same XCD and share its weight rows in that XCD's L2.
+// GEMM kernel rotates and rounds its own tile (fp64, an angle recurrence
+// over each thread's 16 consecutive tokens); otherwise it stores fp32
+// partial tiles plus a few entries of a (cos, sin) table per (token, pair
+// index) -- shared by every rotated head -- and qkv_combine_kernel sums the
+// S partials of each output in split order (deterministic), rotates by the
+// table in fp64 and rounds.  Each output is rounded to bf16 once; the
+// rotation frequencies come from the host.  Workgroup ids are renumbered so
+// the token tiles of one (feature tile, split) run on the same XCD and share
+// its weight rows in that XCD's L2.
 //
 #include "../skv_internal.h"
 #include "bf16_device.h"

@@ -15,7 +15,7 @@ constexpr int kTokBlk = 32;     // query tokens per MFMA block (MFMA n dimension
 constexpr int kRowBlk = 8;      // query blocks per attention row tile (256 rows)
 constexpr int kKeyTile = 64;    // keys staged in LDS per step
 constexpr int kTargetWGs = 256; // one workgroup per compute unit on MI355X
-constexpr int kMinTilesPerSplit = 4;  // key tiles per output-pass split (automatic plan)
+constexpr int kMinTilesPerSplit = 2;  // key tiles per output-pass split (automatic plan)
 constexpr int kMaxPool = 32768; // B + T limit (select keeps the pool in LDS)
 constexpr int kMaxFullSplits = 64;
 

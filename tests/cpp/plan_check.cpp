@@ -91,12 +91,13 @@ int main() {
   skv::Plan p;
   statekv_layer_config c = cfg(28, 4, 128, 256, 4096, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.stat_splits == 18 && p.rt == 7);
-  // small pools: at least 4 key tiles per output split (2B-like: 36 tiles;
-  // 1B-like at B = 1024: 20 tiles); the statistics pass takes twice as many
+  // small pools: at least 2 key tiles per output split (2B-like: 36 tiles;
+  // 1B-like at B = 1024: 20 tiles); the statistics pass takes twice as many,
+  // at most one per key tile
   c = cfg(12, 2, 128, 256, 2048, 65536);
-  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 9 && p.stat_splits == 18 && p.rt == 6);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 18 && p.stat_splits == 36 && p.rt == 6);
   c = cfg(14, 2, 64, 256, 1024, 16384);
-  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 5 && p.stat_splits == 10);
+  CHECK(skv::make_plan(&c, &p) == STATEKV_OK && p.splits == 10 && p.stat_splits == 20);
   c = cfg(28, 4, 96, 256, 4096, 131072);
   CHECK(skv::make_plan(&c, &p) == STATEKV_ERR_UNSUPPORTED);
   c = cfg(28, 5, 128, 256, 4096, 131072);
