@@ -38,6 +38,8 @@ Other measurements (not the headline line):
                        every token, averaged over --mass-frames frames
     --mode frontend    the frame front end (q/k/v projection + RoPE) at the
                        workload's shape, weights read from HBM
+    --mode rope        the library's standalone RoPE launch on one frame's
+                       queries and keys (in place)
 """
 
 from __future__ import annotations
@@ -148,8 +150,9 @@ def state_update_bytes(Hkv, d, T, B, moved_rows, in_place) -> float:
 
 def split_partial_bytes(Hq, Hkv, d, T, plan) -> dict:
     """Bytes the split-K attention writes and reads back beyond the algorithm:
-    per-split row statistics, per-row-tile score partials, per-split O."""
-    stat = plan["stat_splits"] * Hq * T * 2 * 4
+    per-split row statistics (one log-sum-exp per row), per-row-tile score
+    partials, per-split O."""
+    stat = plan["stat_splits"] * Hq * T * 4
     pool_words = plan["key_tiles"] * 64
     score = Hkv * plan["row_tiles"] * pool_words * 4
     S = plan["out_splits"]
@@ -614,6 +617,48 @@ def run_mass(args):
 # the frame front end: q, k, v = rope(X W_Q), rope(X W_K), X W_V
 # ----------------------------------------------------------------------------
 
+def run_rope(args):
+    """Time statekv_rope at the workload's shape: the frame's queries and keys
+    (T x (Hq + Hkv) rows of d bf16) rotated in place at their positions, one
+    call for q and one for k per frame, as a caller that leaves RoPE to the
+    library does.  Algorithmic bytes: every element read and written once."""
+    import torch
+
+    import framegen
+    import streaming_long_video_amd as skv
+
+    spec = framegen.workload(args.workload)
+    T, Hq, Hkv, d = spec.frame_tokens, spec.n_q_heads, spec.n_kv_heads, spec.head_dim
+    dev = torch.device("cuda", 0)
+    layer = skv.Layer(Hq, Hkv, d, T, spec.state_budget, detailed_capacity=T,
+                      rope_theta=spec.rope_theta)
+    g = torch.Generator(device="cpu").manual_seed(spec.seed)
+    q = torch.randn((T, Hq, d), generator=g).to(dev, torch.bfloat16)
+    k = torch.randn((T, Hkv, d), generator=g).to(dev, torch.bfloat16)
+    for i in range(args.warmup + 8):
+        layer.rope(q, i * T)
+        layer.rope(k, i * T)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        layer.rope(q, i * T)
+        layer.rope(k, i * T)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / args.steps
+    layer.close()
+    nbytes = 2 * T * (Hq + Hkv) * d * 2
+    print(json.dumps({
+        "mode": "rope", "workload": args.workload, "tokens": T, "heads": Hq + Hkv,
+        "head_dim": d, "calls_per_frame": 2, "frames": args.steps,
+        "us_per_frame": us, "algorithmic_bytes": nbytes,
+        "achieved_gbs": nbytes / (us * 1e-6) / 1e9,
+        "frac_of_hbm_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "timing": "HIP events around the calls on the launch stream",
+    }), flush=True)
+
+
 def run_frontend(args):
     """Time statekv_qkv_rope at the workload's shape (hidden = Hq * d).  The
     calls cycle through --frontend-layers distinct weight copies (together
@@ -730,7 +775,7 @@ def main(argv=None):
                     help="untimed frames after the state-fill frames (ceil(B/T), never timed)")
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--mode", choices=["headline", "crossover", "depth28", "decode", "mass",
-                                       "frontend"],
+                                       "frontend", "rope"],
                     default="headline")
     ap.add_argument("--decode-queries", type=int, nargs="+", default=[1, 4],
                     help="text tokens per decoding call (decode mode)")
@@ -764,7 +809,8 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     {"headline": run_headline, "crossover": run_crossover, "depth28": run_depth28,
-     "decode": run_decode, "mass": run_mass, "frontend": run_frontend}[args.mode](args)
+     "decode": run_decode, "mass": run_mass, "frontend": run_frontend,
+     "rope": run_rope}[args.mode](args)
 
 
 if __name__ == "__main__":
