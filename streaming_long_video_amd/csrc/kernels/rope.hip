@@ -14,8 +14,10 @@
 // nearly cancel, float cosines would move a small result by several bf16
 // units) -- and the result is rounded once, straight from double, to bf16
 // (nearest, ties to even).
-// One thread owns one (token, pair) and rotates it in every head, so the
-// trigonometry is done once per (token, pair).
+// One thread owns one (token, pair) in kRopeHeads consecutive heads (a
+// second grid dimension covers the heads): the trigonometry is shared by
+// those heads, and every load of the thread is in flight at once.  The
+// frequencies theta^(-2i/d) come from the host.
 #include "../skv_internal.h"
 #include "bf16_device.h"
 
@@ -23,37 +25,53 @@ namespace skv {
 
 namespace {
 
+constexpr int kRopeHeads = 4;  // heads per thread
+
 template <int D>
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs r) {
   constexpr int HALF = D / 2;
   const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (item >= (int64_t)r.n_tokens * HALF) return;
   const int t = (int)(item / HALF), i = (int)(item % HALF);
-  const double inv_freq = pow(r.theta, -2.0 * i / D);
-  const double ang = ((double)(r.first_position + t) / r.scaling) * inv_freq;
-  double s, c;
-  sincos(ang, &s, &c);
+  const int rows = r.n_rows + r.n_rows2;
+  const int hd0 = (int)blockIdx.y * kRopeHeads;
   // rows of the first tensor, then of the second (if any)
-  for (int hd = 0; hd < r.n_rows + r.n_rows2; ++hd) {
+  const uint16_t* src[kRopeHeads];
+  uint16_t* dst[kRopeHeads];
+  float x0[kRopeHeads], x1[kRopeHeads];
+#pragma unroll
+  for (int u = 0; u < kRopeHeads; ++u) {
+    const int hd = min(hd0 + u, rows - 1);
     const bool first = hd < r.n_rows;
     const int row = first ? hd : hd - r.n_rows;
     const int nr = first ? r.n_rows : r.n_rows2;
-    const uint16_t* x = first ? r.x : r.x2;
-    uint16_t* y = first ? r.y : r.y2;
-    const int64_t base = ((int64_t)t * nr + row) * D;
-    const double x0 = bf16_bits_to_f32(x[base + i]);
-    const double x1 = bf16_bits_to_f32(x[base + i + HALF]);
-    y[base + i] = f64_to_bf16_rne(fma(x0, c, -(x1 * s)));
-    y[base + i + HALF] = f64_to_bf16_rne(fma(x0, s, x1 * c));
+    const int64_t base = ((int64_t)t * nr + row) * D + i;
+    src[u] = (first ? r.x : r.x2) + base;
+    dst[u] = (first ? r.y : r.y2) + base;
+    x0[u] = bf16_bits_to_f32(src[u][0]);
+    x1[u] = bf16_bits_to_f32(src[u][HALF]);
+  }
+  const double ang = ((double)(r.first_position + t) / r.scaling) * r.inv_freq[i];
+  double s, c;
+  sincos(ang, &s, &c);
+#pragma unroll
+  for (int u = 0; u < kRopeHeads; ++u) {
+    if (hd0 + u >= rows) break;
+    const double a0 = x0[u], a1 = x1[u];
+    dst[u][0] = f64_to_bf16_rne(fma(a0, c, -(a1 * s)));
+    dst[u][HALF] = f64_to_bf16_rne(fma(a0, s, a1 * c));
   }
 }
 
 }  // namespace
 
-hipError_t launch_rope(const RopeArgs& r, int D, const Stream& st) {
-  const int64_t items = (int64_t)r.n_tokens * (D / 2);
-  if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((items + 255) / 256));
+hipError_t launch_rope(const RopeArgs& args, int D, const Stream& st) {
+  const int64_t items = (int64_t)args.n_tokens * (D / 2);
+  const int rows = args.n_rows + args.n_rows2;
+  if (items == 0 || rows == 0) return hipSuccess;
+  RopeArgs r = args;
+  for (int i = 0; i < D / 2; ++i) r.inv_freq[i] = pow(r.theta, -2.0 * i / D);
+  const dim3 grid((unsigned)((items + 255) / 256), (unsigned)((rows + kRopeHeads - 1) / kRopeHeads));
   if (D == 128)
     hipExtLaunchKernelGGL((rope_kernel<128>), grid, dim3(256), 0, st.st, st.start, st.stop, 0, r);
   else

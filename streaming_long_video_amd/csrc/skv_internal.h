@@ -171,6 +171,7 @@ struct RopeArgs {
   int n_tokens, n_rows, n_rows2;
   int64_t first_position;
   double theta, scaling;
+  double inv_freq[64];  // theta^(-2i/D), filled by launch_rope
 };
 hipError_t launch_rope(const RopeArgs& r, int D, const Stream& st);
 
