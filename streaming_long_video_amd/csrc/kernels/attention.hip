@@ -1,8 +1,9 @@
 // Fused GQA attention over the StateKV candidate pool [C_{n-1} ; frame n] for
 // gfx950.  One kernel template, three passes sharing one tiling:
 //
-//   pass 1 (statistics): per query row, the max and the sum of exp of the
-//     logits over this workgroup's key split (online, per 32-key block);
+//   pass 1 (statistics): per query row, the log-sum-exp of the logits over
+//     this workgroup's key split (a running max and sum per 32-key block,
+//     stored as one float);
 //   pass 2 (output + scores): combines the split statistics into the row
 //     log-sum-exp, recomputes the logits, forms the normalised probabilities
 //     P, accumulates O = P V and the column sums of P (the candidates'
