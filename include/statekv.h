@@ -72,9 +72,10 @@ enum {
    * over every query head of the layer, and every KV head keeps the same
    * positions (rainbus method steps define the importance as a sum over
    * queries without fixing whether heads share one kept set; this is the
-   * per-layer reading).  The state view's score rows stay per KV head.  The
-   * default is per-KV-head selection (paperlayer App. A: sinks kept per layer
-   * and KV head). */
+   * per-layer reading).  The state view's score rows stay per KV head; the
+   * ranked layer-wide value is their fp32 sum in head order.  The default is
+   * per-KV-head selection (paperlayer App. A: sinks kept per layer and KV
+   * head). */
   STATEKV_FLAG_SELECT_SHARED = 1u << 0,
   /* Wrap the detailed cache: token p goes to slot (p - position_offset) mod
    * detailed_capacity.  Without it, a frame that would overflow D fails with

@@ -143,6 +143,8 @@ struct SelectJob {
   int recent;             // keep the last min(pool, budget) entries (most recent)
   InPlace ip;             // ip.pos null: the pool is in position order
   int all_heads;          // the layer-wide job: its selection serves every head
+  int groups;             // row groups summed in turn (the layer-wide job: one per KV head,
+                          // rt rows each, consecutive), 1 otherwise
 };
 
 // In place, the move lists live in LDS past the pool's keys when they fit.
@@ -227,34 +229,44 @@ __device__ void select_one_head(const SelectJob& J, int h) {
   const bool in_place = J.sel && J.ip.pos != nullptr;
   const bool lists_lds = in_place && in_place_lds_fits(pool, J.ip.T);
 
-  // importance = sum of the row tiles' partial column sums, in tile order;
-  // every load of a batch (kLoad candidates x kRows row tiles per thread) is
-  // in flight at once
+  // importance = sum of the row tiles' partial column sums, in tile order
+  // (fp32); the layer-wide job adds the KV heads' sums in head order, so its
+  // value is exactly the fp32 sum of the per-head importances.  Every load of
+  // a batch (kLoad candidates x kRows row tiles per thread) is in flight at
+  // once.
   constexpr int kLoad = 5;  // 5 * 1024 >= 4352: one round at the 8B-like shape
   constexpr int kRows = 8;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int j0 = 0; j0 < pool; j0 += kLoad * kSelThreads) {
-    float acc[kLoad];
+    float tot[kLoad];
+    for (int g = 0; g < J.groups; ++g) {
+      const float* gp = sp + (int64_t)g * J.rt * J.ldsig;
+      float acc[kLoad];
 #pragma unroll
-    for (int q = 0; q < kLoad; ++q) acc[q] = 0.f;
-    for (int r0 = 0; r0 < J.rt; r0 += kRows) {
-      float part[kRows][kLoad];
+      for (int q = 0; q < kLoad; ++q) acc[q] = 0.f;
+      for (int r0 = 0; r0 < J.rt; r0 += kRows) {
+        float part[kRows][kLoad];
 #pragma unroll
-      for (int u = 0; u < kRows; ++u) {
-        // the row's base is uniform, each lane adds a 32-bit byte offset
-        const char* row = reinterpret_cast<const char*>(sp + (int64_t)min(r0 + u, J.rt - 1) * J.ldsig);
+        for (int u = 0; u < kRows; ++u) {
+          // the row's base is uniform, each lane adds a 32-bit byte offset
+          const char* row =
+              reinterpret_cast<const char*>(gp + (int64_t)min(r0 + u, J.rt - 1) * J.ldsig);
 #pragma unroll
-        for (int q = 0; q < kLoad; ++q) {
-          const uint32_t j = (uint32_t)min(j0 + tid + q * kSelThreads, pool - 1);
-          part[u][q] = *reinterpret_cast<const float*>(row + j * 4u);
+          for (int q = 0; q < kLoad; ++q) {
+            const uint32_t j = (uint32_t)min(j0 + tid + q * kSelThreads, pool - 1);
+            part[u][q] = *reinterpret_cast<const float*>(row + j * 4u);
+          }
         }
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+#pragma unroll
+          for (int q = 0; q < kLoad; ++q)
+            if (r0 + u < J.rt) acc[q] = r0 + u == 0 ? part[u][q] : acc[q] + part[u][q];
       }
 #pragma unroll
-      for (int u = 0; u < kRows; ++u)
-#pragma unroll
-        for (int q = 0; q < kLoad; ++q)
-          if (r0 + u < J.rt) acc[q] = r0 + u == 0 ? part[u][q] : acc[q] + part[u][q];
+      for (int q = 0; q < kLoad; ++q) tot[q] = g == 0 ? acc[q] : tot[q] + acc[q];
     }
+    float* acc = tot;
 #pragma unroll
     for (int q = 0; q < kLoad; ++q) {
       const int j = j0 + tid + q * kSelThreads;
@@ -564,9 +576,9 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
                          const Stream& st) {
   shared = shared && !recent;  // the recency window is the same for every head
   SelectJob J = {sig_part, rt, ldsig, pool, budget, scores, ldscores, shared ? nullptr : sel,
-                 ldsel, recent ? 1 : 0, ip, 0};
+                 ldsel, recent ? 1 : 0, ip, 0, 1};
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
-  SelectJob J2 = {sig_part, rt * hkv, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1};
+  SelectJob J2 = {sig_part, rt, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1, hkv};
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0};
   // The O sum runs beside the selection: enough workgroups that it ends
   // before the selection (about 18 partial loads per thread: two f32x4

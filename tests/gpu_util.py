@@ -121,6 +121,15 @@ def teacher_forced_frame(orc, layer, n, q, k, v, o_gpu_dev=None) -> FrameReport:
     frame_pos = layer.position_offset + n * q.shape[0] + np.arange(q.shape[0], dtype=np.int64)
     score_err = 0.0
     match = total = 0
+    shared_rule = None
+    if flags & FLAG_SELECT_SHARED and not flags & FLAG_SELECT_RECENT:
+        # the layer-wide importance is the fp32 sum of the per-head rows in
+        # head order (every head holds the same rows, so one pool serves)
+        tot = after.scores[0].astype(np.float32)
+        for h in range(1, len(ref.scores)):
+            tot = (tot + after.scores[h].astype(np.float32)).astype(np.float32)
+        pool0 = np.concatenate([before.pos[0], frame_pos])
+        shared_rule = pool0[select_top_b(tot.astype(np.float64), pool0, layer.B)]
     for h in range(len(ref.scores)):
         np.testing.assert_array_equal(ref.pool_positions[h].shape[0], after.pool)
         # the GPU's pool is [its state rows as held ; frame]; the oracle's ascends
@@ -139,7 +148,7 @@ def teacher_forced_frame(orc, layer, n, q, k, v, o_gpu_dev=None) -> FrameReport:
         elif not flags & FLAG_SELECT_SHARED:
             rule = gpu_pool[select_top_b(after.scores[h].astype(np.float64), gpu_pool, layer.B)]
         else:
-            rule = None  # the layer-wide sum is not one of the per-head rows
+            rule = shared_rule
         if rule is not None:
             assert sorted(kept_gpu) == sorted(rule.tolist()), (n, h, "selection rule")
         if flags & FLAG_SLOT_STABLE:
