@@ -258,12 +258,17 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a) {
 
 // Merge of the workgroup partials of one output row (text token t, query head
 // g) over a 32-column slice: M = max_p m_p, w_p = 2^((m_p - M) c),
-// O = sum_p w_p O_p / sum_p w_p l_p.  Threads stride over the partials for the
-// max and the weights; thread (column, part) sums every 8th partial; all
-// reductions run in a fixed order.
+// O = sum_p w_p O_p / sum_p w_p l_p.  Thread (column, part) sums every 8th
+// partial; all reductions run in a fixed order.  The row's m and l partials
+// and each thread's first kEarly O partials are loaded together, before the
+// weights are known, so the merge waits for one memory round trip rather
+// than three.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int parts, float* o) {
-  constexpr int kParts = 8;  // 256 threads = 32 columns x 8
+  constexpr int kParts = 8;   // 256 threads = 32 columns x 8
+  constexpr int kEarly = 24;  // O partials per thread loaded with m and l
+  constexpr int kMl = kMaxDecodeParts / 256;  // m and l partials per thread
+  static_assert(kMl * 256 == kMaxDecodeParts, "m and l partials split evenly");
   __shared__ float wsh[kMaxDecodeParts];
   __shared__ float red[8];
   __shared__ float osum[kParts][32];
@@ -272,12 +277,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int par
   const int row = blockIdx.x / (D / 32);
   const int g = row % a.Hq, t = row / a.Hq;
   const float sl2 = a.scale_log2;
-  float mloc = -INFINITY;
-  for (int p = tid; p < parts; p += 256) {
-    const float m = a.m_part[((int64_t)p * a.Hq + g) * a.M + t];
-    wsh[p] = m;
-    mloc = fmaxf(mloc, m);
+  const int c = tid % 32, part = tid / 32;
+  const float* src = a.o_part + ((int64_t)t * a.Hq + g) * D + chunk * 32 + c;
+  const int64_t pstride = (int64_t)a.M * a.Hq * D;
+  float early[kEarly], mv[kMl], lv[kMl];
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    const int p = part + u * kParts;
+    early[u] = p < parts ? src[p * pstride] : 0.f;
   }
+#pragma unroll
+  for (int u = 0; u < kMl; ++u) {
+    const int p = tid + 256 * u;
+    const int64_t i = ((int64_t)p * a.Hq + g) * a.M + t;
+    mv[u] = p < parts ? a.m_part[i] : -INFINITY;
+    lv[u] = p < parts ? a.l_part[i] : 0.f;
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kMl; ++u) mloc = fmaxf(mloc, mv[u]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
   if (lane == 0) red[wv] = mloc;
@@ -285,23 +303,29 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a, int par
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float msafe = M == -INFINITY ? 0.f : M;
   float lloc = 0.f;
-  for (int p = tid; p < parts; p += 256) {
-    const float m = wsh[p];
-    const float wp = m == -INFINITY ? 0.f : exp2f((m - msafe) * sl2);
-    wsh[p] = wp;
-    lloc += wp * a.l_part[((int64_t)p * a.Hq + g) * a.M + t];
+#pragma unroll
+  for (int u = 0; u < kMl; ++u) {
+    const int p = tid + 256 * u;
+    if (p < parts) {
+      const float wp = mv[u] == -INFINITY ? 0.f : exp2f((mv[u] - msafe) * sl2);
+      wsh[p] = wp;
+      lloc += wp * lv[u];
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off);
   if (lane == 0) red[4 + wv] = lloc;
   __syncthreads();
   const float L = (red[4] + red[5]) + (red[6] + red[7]);
-  const int c = tid % 32, part = tid / 32;
-  const float* src = a.o_part + ((int64_t)t * a.Hq + g) * D + chunk * 32 + c;
-  const int64_t pstride = (int64_t)a.M * a.Hq * D;
   float acc = 0.f;
-  // groups of 8 independent loads, summed in partial order
-  for (int p0 = part; p0 < parts; p0 += 8 * kParts) {
+#pragma unroll
+  for (int u = 0; u < kEarly; ++u) {
+    const int p = part + u * kParts;
+    if (p < parts) acc += wsh[p] * early[u];
+  }
+  // the rest (more than 8 kEarly partials): groups of 8 independent loads,
+  // summed in partial order
+  for (int p0 = part + kEarly * kParts; p0 < parts; p0 += 8 * kParts) {
     float vals[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
