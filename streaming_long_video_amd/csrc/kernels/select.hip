@@ -209,6 +209,7 @@ struct SumJob {
   int64_t n4;
   int S;
   int bf16;
+  int delay;  // s_sleep(32) rounds (about 0.85 us each at 2.4 GHz) before the sum starts
 };
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -509,7 +510,8 @@ __device__ void append_frame(const AppendJob& A, int blk, int nblk) {
 // the whole layer from the scores summed over every KV head (J2: the
 // Hkv x rt partial rows read as one list, h-major); the next n_append blocks
 // append the frame to the detailed cache; the remaining blocks sum the split
-// O partials (grid-stride over their share).
+// O partials (grid-stride over their share; with a short sleep first when a
+// selection runs beside them, see launch_select).
 __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, int n_select,
                                                                  SelectJob J2, int n_shared,
                                                                  AppendJob A, int n_append,
@@ -528,6 +530,7 @@ __global__ __launch_bounds__(kSelThreads) void select_sum_kernel(SelectJob J, in
     return;
   }
   n_select += n_append;
+  for (int i = 0; i < Sj.delay; ++i) __builtin_amdgcn_s_sleep(32);
   const int64_t nb = gridDim.x - n_select;
   for (int64_t i = (int64_t)(blockIdx.x - n_select) * kSelThreads + threadIdx.x; i < Sj.n4;
        i += nb * kSelThreads) {
@@ -579,7 +582,14 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
                  ldsel, recent ? 1 : 0, ip, 0, 1};
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
   SelectJob J2 = {sig_part, rt, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1, hkv};
-  SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0};
+  // When a selection runs, the O sum starts one sleep round late: the
+  // selecting workgroups first read their heads' partial column sums, and
+  // the sum's tens of megabytes of split partials would otherwise fill the
+  // memory queues under those reads (at the 8B-like shape the launch takes
+  // 12.2 us instead of 12.9; two rounds are no better, three make the sum
+  // the long pole).
+  const int delay = (pool > budget && !recent) ? 1 : 0;
+  SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0, delay};
   // The O sum runs beside the selection: enough workgroups that it ends
   // before the selection (about 18 partial loads per thread: two f32x4
   // outputs of 9 splits at the 8B-like shape, one output when there are more
