@@ -582,13 +582,16 @@ hipError_t launch_select(const float* sig_part, int rt, int ldsig, int hkv, int 
                  ldsel, recent ? 1 : 0, ip, 0, 1};
   // the layer-wide job: every head holds the same rows, so head 0's positions serve
   SelectJob J2 = {sig_part, rt, ldsig, pool, budget, nullptr, 0, sel, ldsel, 0, ip, 1, hkv};
-  // When a selection runs, the O sum starts one sleep round late: the
-  // selecting workgroups first read their heads' partial column sums, and
-  // the sum's tens of megabytes of split partials would otherwise fill the
-  // memory queues under those reads (at the 8B-like shape the launch takes
-  // 12.2 us instead of 12.9; two rounds are no better, three make the sum
-  // the long pole).
-  const int delay = (pool > budget && !recent) ? 1 : 0;
+  // When a selection runs and the O sum has slack, the sum starts one sleep
+  // round late: the selecting workgroups first read their heads' partial
+  // column sums, and the sum's tens of megabytes of split partials would
+  // otherwise fill the memory queues under those reads.  The slack is judged
+  // by the split partials per pool candidate: 7.6 KB at the 8B-like shape
+  // (the launch takes 12.2 us instead of 12.9; two rounds are no better,
+  // three make the sum the long pole), 12.3 KB in the 2B-like 28-layer
+  // stream, where starting late already makes it the long pole (+1.5 %).
+  const double part_per_candidate = (double)S * (double)o_elems * 4.0 / (double)pool;
+  const int delay = (pool > budget && !recent && part_per_candidate < 10240.0) ? 1 : 0;
   SumJob Sj = {reinterpret_cast<const f32x4*>(o_part), o, o_elems / 4, S, o_bf16 ? 1 : 0, delay};
   // The O sum runs beside the selection: enough workgroups that it ends
   // before the selection (about 18 partial loads per thread: two f32x4
