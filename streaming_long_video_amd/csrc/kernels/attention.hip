@@ -83,6 +83,20 @@ __device__ inline int xcd_logical_id(int b, int n) {
   return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
 }
 
+// The same ranges with the dispatch order inside each XCD changed so that
+// the logical ids of the last key split (lid % S == S - 1, the split holding
+// the frame's masked tiles, the slowest) come first, then the others in
+// order: workgroups start over about 2 us in dispatch order.
+__device__ inline int xcd_logical_id_last_split_first(int b, int n, int S) {
+  const int q = n >> 3, r = n & 7, x = b & 7, i = b >> 3;
+  const int L0 = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  const int len = x < r ? q + 1 : q;
+  const int o = (S - 1 - L0 % S) % S;  // first last-split id: L0 + o
+  const int nf = len > o ? (len - o - 1) / S + 1 : 0;
+  if (i < nf) return L0 + o + i * S;
+  const int j = i - nf;  // the j-th of the other ids (S > 1 here)
+  return L0 + (j < o ? j : j + 1 + (j - o) / (S - 1));
+}
 __device__ inline float as_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ inline int as_i(float x) { return __builtin_bit_cast(int, x); }
 
@@ -309,13 +323,16 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, half = lane >> 5;
-  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int lid = PASS == 2 ? xcd_logical_id_last_split_first(blockIdx.x, gridDim.x, a.S)
+                            : xcd_logical_id(blockIdx.x, gridDim.x);
   // The statistics pass gives consecutive logical ids the row tiles of one
   // key split (they share K tiles in L2).  The output pass gives them the key
   // splits of one row tile instead: its prologue reads the row tile's queries
   // and every split's statistics, a burst that then stays within one XCD
   // (1.3 us faster at the 8B shape; the same order makes the statistics pass
-  // slower).
+  // slower).  In both passes the last key split (the frame's masked tiles,
+  // the slowest workgroups) is dispatched first: 0.8 % off the 2B-like
+  // 28-layer stream, neutral at the 8B-like shape.
   int rtile, s, h;
   if (PASS == 2) {
     s = lid % a.S;
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(kThreads, PASS == 1 ? 4 : 2) void attn_kernel(AttnA
   } else {
     rtile = lid % a.rt;
     const int hs = lid / a.rt;
-    s = hs % a.S;
+    s = a.S - 1 - hs % a.S;  // splits in reverse: each head's last split first
     h = hs / a.S;
   }
   const int c = a.c;
